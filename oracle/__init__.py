@@ -1,0 +1,294 @@
+"""CPU oracle for the Beam MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and `bench.py`'s CPU-baseline leg may
+import this package.  It shares no code with the GPU library
+(`sparse_mixture_experts_group_amd`) and never imports it; the only module both
+use is `beam_inputs`, which makes the seeded input bytes.
+
+What the layer computes (Reflection Beam 1.0 overview, section "Mixture of
+Experts: 256 experts, 8 routed per token"; the residual and norm sublayer from
+section "Residual stream: depth-dependent weights keep the hidden state at
+constant scale"):
+
+  router   z = x . Wr (+ b);  s = sigmoid(z)                        FP32 (C)
+  groups   score_g = top1 + top2 of s inside group g; keep Kg       FP32 (C)
+  experts  top-K of s inside the kept groups; w_i = alpha s_i / sum  FP32 (C)
+  experts  a = SiLU(x Wg^T) * (x Wu^T);  o = a Wd^T                  float64
+  combine  y = sum_i w_i o_i                                          float64
+  sublayer h' = sqrt((k-1)/k) h + (1/sqrt k) RMSNorm(y),
+           with the MoE input RMSNorm(h) (FP32, C)                    float64
+
+The router and the pre-norm are FP32 because the pages fix those sites to FP32
+and their result decides integers (expert ids); every other step is float64, a
+tighter reference than the FP32 floor the pages set.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "beam_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libbeam_oracle.so")
+GCC_FLAGS = ["-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+             "-fno-fast-math", "-mfma", "-mavx2", "-Wall"]
+
+
+def build() -> str:
+    """Compile oracle/beam_oracle.c into oracle/libbeam_oracle.so (gcc)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64 = ctypes.c_int64
+        L.oracle_expf.restype = ctypes.c_float
+        L.oracle_expf.argtypes = [ctypes.c_float]
+        L.oracle_sigmoidf.restype = ctypes.c_float
+        L.oracle_sigmoidf.argtypes = [ctypes.c_float]
+        L.oracle_expf_array.argtypes = [i64, f32p, f32p]
+        L.oracle_sigmoidf_array.argtypes = [i64, f32p, f32p]
+        L.oracle_router_logits.argtypes = [i64, ctypes.c_int, ctypes.c_int, f32p, f32p, f32p, f32p]
+        L.oracle_route.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_float, f32p, i32p, f32p, f32p, f32p, i32p]
+        L.oracle_prenorm.argtypes = [i64, ctypes.c_int, f32p, f32p, ctypes.c_float, f32p, f32p]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _f32p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _i32p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+# ---------------------------------------------------------------------------
+# storage-format decoding (the oracle's own; never shared with the GPU side)
+# ---------------------------------------------------------------------------
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 exactly (bf16 = upper half of an fp32)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of each of the 256 OCP FP8 E4M3FN codes (OCP 8-bit Floating Point
+    Specification v1.0): sign bit, 4-bit exponent (bias 7), 3-bit mantissa;
+    exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; no infinity."""
+    tab = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        ex = (c >> 3) & 0xF
+        m = c & 0x7
+        if ex == 0xF and m == 0x7:
+            tab[c] = np.nan
+        elif ex == 0:
+            tab[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            tab[c] = sign * (1.0 + m / 8.0) * 2.0 ** (ex - 7)
+    return tab
+
+
+E4M3_TABLE = _e4m3_table()
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    return E4M3_TABLE[np.asarray(codes, np.uint8)]
+
+
+def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
+    """Stored value of a block-scaled E4M3 matrix: code value * its tile's FP32 scale
+    (exact in float64)."""
+    v = e4m3_to_f64(codes)
+    n, k = v.shape
+    return (v.reshape(n // block, block, k // block, block)
+            * scales.astype(np.float64)[:, None, :, None]).reshape(n, k)
+
+
+# ---------------------------------------------------------------------------
+# FP32 router (C)
+# ---------------------------------------------------------------------------
+def expf(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    y = np.empty_like(x)
+    lib().oracle_expf_array(x.size, _f32p(x), _f32p(y))
+    return y
+
+
+def sigmoidf(z: np.ndarray) -> np.ndarray:
+    z = np.ascontiguousarray(z, np.float32)
+    s = np.empty_like(z)
+    lib().oracle_sigmoidf_array(z.size, _f32p(z), _f32p(s))
+    return s
+
+
+def router_logits(x32: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None = None):
+    """z [T,E] FP32: one fused multiply-add chain per (t, e) over h ascending, then + b[e]."""
+    x32 = np.ascontiguousarray(x32, np.float32)
+    wr = np.ascontiguousarray(w_router, np.float32)
+    T, H = x32.shape
+    H2, E = wr.shape
+    assert H == H2
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    z = np.empty((T, E), np.float32)
+    lib().oracle_router_logits(T, H, E, _f32p(x32), _f32p(wr), _f32p(b), _f32p(z))
+    return z
+
+
+def route(z: np.ndarray, G: int, Kg: int, K: int, alpha: float, details: bool = False):
+    """Group-limited top-K of sigmoid scores.  Returns ids [T,K] int32 (score
+    descending, ties to the lower index) and weights [T,K] FP32 (sum = alpha)."""
+    z = np.ascontiguousarray(z, np.float32)
+    T, E = z.shape
+    assert E % G == 0 and E // G >= 2 and 1 <= Kg <= G and 1 <= K <= Kg * (E // G)
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float32)
+    s = np.empty((T, E), np.float32) if details else None
+    gs = np.empty((T, G), np.float32) if details else None
+    gk = np.empty((T, Kg), np.int32) if details else None
+    lib().oracle_route(T, E, G, Kg, K, float(alpha), _f32p(z), _i32p(ids), _f32p(w),
+                       _f32p(s), _f32p(gs), _i32p(gk))
+    if details:
+        return ids, w, {"scores": s, "group_scores": gs, "kept_groups": gk}
+    return ids, w
+
+
+def prenorm(h32: np.ndarray, gain: np.ndarray | None, eps: float):
+    """FP32 RMSNorm with the fixed summation order; returns (xhat [T,H], rstd [T])."""
+    h32 = np.ascontiguousarray(h32, np.float32)
+    T, H = h32.shape
+    g = None if gain is None else np.ascontiguousarray(gain, np.float32)
+    out = np.empty_like(h32)
+    r = np.empty(T, np.float32)
+    lib().oracle_prenorm(T, H, _f32p(h32), _f32p(g), float(eps), _f32p(out), _f32p(r))
+    return out, r
+
+
+# ---------------------------------------------------------------------------
+# expert MLPs, combine, post-norm, residual (float64)
+# ---------------------------------------------------------------------------
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) (float64)."""
+    return g / (1.0 + np.exp(-g))
+
+
+def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """SwiGLU expert on rows [n,H] (float64): a = SiLU(x Wg^T) * (x Wu^T), o = a Wd^T.
+    w13 [2I,H]: gate rows 0..I-1, up rows I..2I-1; w2 [H,I]."""
+    I = w13.shape[0] // 2
+    g = xrows @ w13[:I].T
+    u = xrows @ w13[I:].T
+    a = silu(g) * u
+    return a @ w2.T
+
+
+class ExpertBank:
+    """Float64 view of stored expert weights, decoded one expert at a time."""
+
+    def __init__(self, w13, w2, dtype: str, w13_scale=None, w2_scale=None, block: int = 128):
+        self.w13, self.w2, self.dtype = w13, w2, dtype
+        self.s13, self.s2, self.block = w13_scale, w2_scale, block
+
+    def expert(self, e: int):
+        if self.dtype == "f32":
+            return self.w13[e].astype(np.float64), self.w2[e].astype(np.float64)
+        if self.dtype == "bf16":
+            return (bf16_to_f32(self.w13[e]).astype(np.float64),
+                    bf16_to_f32(self.w2[e]).astype(np.float64))
+        if self.dtype == "fp8_e4m3":
+            return (dequant_blocks(self.w13[e], self.s13[e], self.block),
+                    dequant_blocks(self.w2[e], self.s2[e], self.block))
+        raise ValueError(self.dtype)
+
+
+def moe_combine(x64: np.ndarray, ids: np.ndarray, w: np.ndarray, bank: ExpertBank,
+                return_expert_outputs: bool = False):
+    """y[t] = sum_{i=0..K-1} w[t,i] * FFN_{ids[t,i]}(x[t]) in float64.
+
+    Loops expert by expert (each expert's rows at once) -- the per-token definition
+    is unchanged; the loop order only keeps one expert's weights decoded at a time.
+    The sum over i is taken in ascending i.
+    """
+    T, K = ids.shape
+    H = x64.shape[1]
+    outs = np.zeros((T, K, H), np.float64)
+    for e in np.unique(ids):
+        t_idx, k_idx = np.nonzero(ids == e)
+        w13, w2 = bank.expert(int(e))
+        outs[t_idx, k_idx] = expert_ffn(x64[t_idx], w13, w2)
+    y = np.zeros((T, H), np.float64)
+    for i in range(K):
+        y += w[:, i:i + 1].astype(np.float64) * outs[:, i]
+    if return_expert_outputs:
+        return y, outs
+    return y
+
+
+def rmsnorm64(y: np.ndarray, gain: np.ndarray | None, eps: float) -> np.ndarray:
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+    out = y * r
+    if gain is not None:
+        out = out * gain.astype(np.float64)
+    return out
+
+
+def residual_coeffs(k: int):
+    """Constant-scale residual at step k: keep sqrt((k-1)/k) of the stream, add
+    1/sqrt(k) of the sublayer output (Reflection Beam 1.0 overview, "Residual stream")."""
+    return math.sqrt((k - 1) / k), 1.0 / math.sqrt(k)
+
+
+def residual_update(h64: np.ndarray, out64: np.ndarray, k: int) -> np.ndarray:
+    c1, c2 = residual_coeffs(k)
+    return c1 * h64 + c2 * out64
+
+
+# ---------------------------------------------------------------------------
+# whole layer / sublayer
+# ---------------------------------------------------------------------------
+def moe_forward(x32: np.ndarray, w_router, bias, bank: ExpertBank, G, Kg, K, alpha,
+                token_subset: np.ndarray | None = None):
+    """One MoE layer on FP32 activations x32 [T,H].  Routing runs for every token;
+    the expert MLPs and the combine run for `token_subset` (all tokens if None).
+    Returns dict(ids, w, y [n,H] float64, tokens)."""
+    z = router_logits(x32, w_router, bias)
+    ids, w = route(z, G, Kg, K, alpha)
+    tok = np.arange(x32.shape[0]) if token_subset is None else np.asarray(token_subset)
+    y = moe_combine(x32[tok].astype(np.float64), ids[tok], w[tok], bank)
+    return {"ids": ids, "w": w, "y": y, "tokens": tok, "logits": z}
+
+
+def sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, eps: float,
+                     w_router, bias, bank: ExpertBank, G, Kg, K, alpha,
+                     token_subset: np.ndarray | None = None):
+    """pre-RMSNorm (FP32, fixed order) -> MoE -> post-RMSNorm -> constant-scale residual.
+    Returns dict(ids, w, y (MoE output), h_new (float64), tokens)."""
+    xhat, _ = prenorm(h32, pre_gain, eps)
+    r = moe_forward(xhat, w_router, bias, bank, G, Kg, K, alpha, token_subset)
+    tok = r["tokens"]
+    yn = rmsnorm64(r["y"], post_gain, eps)
+    r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)
+    r["xhat"] = xhat
+    return r

@@ -1,0 +1,62 @@
+"""Checks of the seeded input generator (beam_inputs) against independent routines."""
+import numpy as np
+import torch
+
+import oracle
+from beam_inputs import (WORKLOADS, encode_e4m3, make_inputs, quantize_e4m3_blocks, to_bf16_bits,
+                         token_inputs, zipf_logit_offsets, normal)
+
+
+def test_bf16_rounding_matches_torch():
+    rs = np.random.default_rng(0)
+    a = (rs.standard_normal(1_000_000) * np.exp(rs.uniform(-20, 20, 1_000_000))).astype(np.float32)
+    mine = to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_e4m3_encoding_matches_torch_rne_saturating():
+    rs = np.random.default_rng(1)
+    v = (rs.standard_normal(500_000) * np.exp(rs.uniform(-8, 6, 500_000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    mine = encode_e4m3(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    # every finite code round-trips
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle.e4m3_to_f64(codes).astype(np.float32)
+    rt = encode_e4m3(vals)
+    assert np.array_equal(oracle.e4m3_to_f64(rt), oracle.e4m3_to_f64(codes))
+
+
+def test_block_quantisation_amax_maps_to_448():
+    w = normal(0, (5,), (256, 384), std=0.02)
+    codes, scales = quantize_e4m3_blocks(w, 128)
+    assert scales.shape == (2, 3)
+    deq = oracle.dequant_blocks(codes, scales, 128)
+    for i in range(2):
+        for j in range(3):
+            blk = np.abs(deq[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128])
+            assert np.isclose(blk.max(), 448 * scales[i, j], rtol=0)
+    rel = np.abs(deq - w) / np.abs(w).max()
+    assert rel.max() <= 2.0 ** -4 + 1e-6      # half a step of a 3-bit mantissa at amax
+
+
+def test_prefix_rows_independent_of_T():
+    w = WORKLOADS["beam_prefill_t4096"]
+    a = token_inputs(w.with_T(16))
+    b = token_inputs(w.with_T(40))
+    assert np.array_equal(a, b[:16])
+
+
+def test_zipf_offsets_skew():
+    b = zipf_logit_offsets(256, 1.1, 0)
+    p = np.exp(b.astype(np.float64)) / 256
+    assert abs(p.sum() - 1) < 1e-5
+    assert b.max() > 3.9 and b.min() < -2.0
+
+
+def test_tiny_inputs_shapes():
+    inp = make_inputs(WORKLOADS["tiny_f32"])
+    assert inp.x.shape == (64, 128) and inp.x.dtype == np.float32
+    assert inp.w13.shape == (16, 128, 128) and inp.w2.shape == (16, 128, 64)

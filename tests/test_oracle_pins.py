@@ -1,0 +1,429 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test states what fixes the expected value: a closed form, a textbook or
+library routine, a brute-force enumeration, an exact rational computation, or a
+number printed on the pages (tests/golden/beam_page_facts.json).  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from beam_inputs import WORKLOADS, make_inputs, normal
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers that do exact arithmetic independently of the oracle
+# ---------------------------------------------------------------------------
+def round_f32(q: Fraction) -> float:
+    """Round an exact rational to the nearest float32 (ties to even), no double rounding."""
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    m = a / quantum
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(fl * quantum)
+
+
+def fma_f32(a, b, c) -> float:
+    return round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def ulp32(x: np.ndarray) -> np.ndarray:
+    """ulp of a float32 at |x| (normal range)."""
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, e - 24)
+
+
+# ---------------------------------------------------------------------------
+# exp / sigmoid
+# ---------------------------------------------------------------------------
+def test_exp_within_2ulp_of_double_exp_strided_sweep():
+    """Own FP32 exp vs float64 exp: <= 2 ulp over a strided sweep of every FP32 in
+    [-87, 87] (every 13th bit pattern: ~170M values)."""
+    hi = np.float32(87.0).view(np.uint32)
+    worst = 0.0
+    for sign in (0, 0x80000000):
+        for start in range(0, int(hi) + 1, 13 * (1 << 22)):
+            bits = np.arange(start, min(start + 13 * (1 << 22), int(hi) + 1), 13, dtype=np.uint32)
+            x = (bits | np.uint32(sign)).view(np.float32)
+            y = oracle.expf(x).astype(np.float64)
+            ref = np.exp(x.astype(np.float64))
+            err = np.abs(y - ref) / ulp32(ref)
+            worst = max(worst, float(err.max()))
+    assert worst <= 2.0, worst
+
+
+def test_exp_dense_near_zero_and_special_values():
+    x = np.linspace(-1, 1, 2_000_001, dtype=np.float32)
+    y = oracle.expf(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    assert (np.abs(y - ref) / ulp32(ref)).max() <= 2.0
+    assert oracle.expf(np.array([0.0], np.float32))[0] == 1.0
+    # clamp: values beyond +-87 behave as +-87, results stay normal and finite
+    big = oracle.expf(np.array([87.0, 1000.0, -87.0, -1000.0], np.float32))
+    assert big[0] == big[1] and big[2] == big[3]
+    assert np.isfinite(big).all() and big[2] >= np.finfo(np.float32).tiny
+
+
+def test_sigmoid_closed_forms():
+    s = oracle.sigmoidf(np.array([0.0, math.log(3.0), -math.log(3.0)], np.float32))
+    assert s[0] == 0.5                                   # sigma(0) = 1/2 exactly
+    assert abs(s[1] - 0.75) < 2e-7 and abs(s[2] - 0.25) < 2e-7
+    z = np.linspace(-30, 30, 100001, dtype=np.float32)
+    ref = 1.0 / (1.0 + np.exp(-z.astype(np.float64)))
+    got = oracle.sigmoidf(z).astype(np.float64)
+    assert (np.abs(got - ref) / ref).max() < 4e-7
+    # symmetry sigma(z) + sigma(-z) = 1
+    assert np.abs(got + oracle.sigmoidf(-z).astype(np.float64) - 1.0).max() < 2e-7
+
+
+# ---------------------------------------------------------------------------
+# router logits
+# ---------------------------------------------------------------------------
+def test_logits_are_one_fused_chain_in_ascending_h_exact_rationals():
+    """Bit-exact against exact rational emulation of acc = fma(x_h, w_h, acc), h
+    ascending, then + bias (one rounding each)."""
+    rs = np.random.default_rng(7)
+    T, H, E = 3, 24, 5
+    x = rs.standard_normal((T, H)).astype(np.float32)
+    w = rs.standard_normal((H, E)).astype(np.float32)
+    b = rs.standard_normal(E).astype(np.float32)
+    z = oracle.router_logits(x, w, b)
+    for t in range(T):
+        for e in range(E):
+            acc = 0.0
+            for h in range(H):
+                acc = fma_f32(x[t, h], w[h, e], acc)
+            acc = round_f32(Fraction(acc) + Fraction(float(b[e])))
+            assert z[t, e] == np.float32(acc), (t, e)
+
+
+def test_logits_within_rounding_bound_of_exact_dot():
+    """|z - exact| <= gamma_H * sum |x w| (standard error bound of a length-H
+    floating-point dot product)."""
+    w = WORKLOADS["beam_decode_t16"]
+    x = normal(0, (99,), (8, w.H))
+    wr = normal(0, (98,), (w.H, w.E), std=1 / math.sqrt(w.H))
+    z = oracle.router_logits(x, wr).astype(np.float64)
+    exact = x.astype(np.float64) @ wr.astype(np.float64)
+    u = 2.0 ** -24
+    gamma = w.H * u / (1 - w.H * u)
+    bound = gamma * (np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64)))
+    assert (np.abs(z - exact) <= bound).all()
+
+
+# ---------------------------------------------------------------------------
+# group-limited selection
+# ---------------------------------------------------------------------------
+def brute_route(s: np.ndarray, G: int, Kg: int, K: int):
+    """Brute force for one token: group score = best pair sum in the group (max over
+    all pairs i<j of fl(s_i + s_j)), kept groups and experts by enumerating every
+    subset and taking the one whose members, sorted by (value desc, index asc),
+    form the lexicographically best sequence."""
+    E = s.size
+    S = E // G
+    gs = []
+    for g in range(G):
+        vals = s[g * S:(g + 1) * S]
+        gs.append(max(np.float32(vals[i] + vals[j]) for i in range(S) for j in range(i + 1, S)))
+
+    def key(items, val):
+        return sorted(((-float(val[i]), i) for i in items))
+
+    best_groups = min(itertools.combinations(range(G), Kg), key=lambda c: key(c, gs))
+    cand = [e for e in range(E) if e // S in best_groups]
+    best_exp = min(itertools.combinations(cand, K), key=lambda c: key(c, s))
+    ordered = [i for _, i in key(best_exp, s)]
+    return ordered, sorted(best_groups, key=lambda g: (-float(gs[g]), g))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_matches_brute_force_tiny_layer(seed):
+    w = WORKLOADS["tiny_f32"]
+    rs = np.random.default_rng(seed)
+    T = 48
+    z = rs.standard_normal((T, w.E)).astype(np.float32)
+    if seed % 2:          # force exact ties across and within groups
+        z = np.round(z * 2) / 2
+    ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True)
+    s = d["scores"]
+    for t in range(T):
+        exp_ids, exp_groups = brute_route(s[t], w.G, w.Kg, w.K)
+        assert list(ids[t]) == exp_ids, (t, ids[t], exp_ids)
+        assert list(d["kept_groups"][t]) == exp_groups
+
+
+def dominance_ok(s, gs, kept, ids, G, K):
+    E = s.size
+    S = E // G
+    order = lambda v, i: (-float(v), i)
+    keptset = set(int(g) for g in kept)
+    for g in keptset:
+        for h in set(range(G)) - keptset:
+            if not order(gs[g], g) < order(gs[h], h):
+                return False
+    chosen = set(int(e) for e in ids)
+    cand = [e for e in range(E) if e // S in keptset]
+    for e in chosen:
+        if e // S not in keptset:
+            return False
+        for f in set(cand) - chosen:
+            if not order(s[e], e) < order(s[f], f):
+                return False
+    seq = [order(s[e], e) for e in ids]
+    return seq == sorted(seq) and len(chosen) == K
+
+
+def test_route_dominance_certificate_beam_size():
+    w = WORKLOADS["beam_prefill_t4096"]
+    rs = np.random.default_rng(3)
+    T = 256
+    z = rs.standard_normal((T, w.E)).astype(np.float32)
+    ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True)
+    s, gs, kept = d["scores"], d["group_scores"], d["kept_groups"]
+    for t in range(T):
+        # group scores: independent recomputation via a sort
+        grp = np.sort(s[t].reshape(w.G, -1), axis=1)
+        assert np.array_equal(gs[t], (grp[:, -1] + grp[:, -2]).astype(np.float32))
+        assert dominance_ok(s[t], gs[t], kept[t], ids[t], w.G, w.K)
+    # group choice brute-forced over all C(8,4) = 70 subsets
+    for t in range(0, T, 17):
+        best = min(itertools.combinations(range(w.G), w.Kg),
+                   key=lambda c: sorted((-float(gs[t][g]), g) for g in c))
+        assert sorted(best) == sorted(kept[t])
+
+
+def test_route_all_ties_closed_form():
+    """Wr = 0 -> every score is sigma(0) = 0.5 -> groups 0..Kg-1, experts 0..K-1,
+    every weight exactly alpha / K."""
+    for name in ("tiny_f32", "beam_decode_t16"):
+        w = WORKLOADS[name]
+        z = oracle.router_logits(np.ones((4, w.H), np.float32), np.zeros((w.H, w.E), np.float32))
+        ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True)
+        assert (ids == np.arange(w.K)).all()
+        assert (d["kept_groups"] == np.arange(w.Kg)).all()
+        assert (wts == np.float32(w.alpha / w.K)).all()
+
+
+def test_route_single_group_is_plain_topk():
+    """G = 1 (or Kg = G) reduces to plain top-K over all experts: compare with a
+    stable numpy sort on (-s, index)."""
+    rs = np.random.default_rng(11)
+    z = np.round(rs.standard_normal((64, 32)).astype(np.float32) * 4) / 4
+    for G, Kg in ((1, 1), (4, 4)):
+        ids, _, d = oracle.route(z, G, Kg, 6, 2.5, details=True)
+        s = d["scores"]
+        ref = np.argsort(-s, axis=1, kind="stable")[:, :6]
+        assert np.array_equal(ids, ref)
+
+
+def test_route_top2_sum_not_max():
+    """A group with the single highest score but a weak runner-up loses to a group
+    with two strong scores."""
+    E, G = 16, 4
+    z = np.full((1, E), -5.0, np.float32)
+    z[0, 0] = 4.0          # group 0: max 4.0, runner-up -5
+    z[0, 4] = 3.0          # group 1: 3.0 + 3.0
+    z[0, 5] = 3.0
+    ids, _, d = oracle.route(z, G, 1, 2, 2.5, details=True)
+    assert list(d["kept_groups"][0]) == [1]
+    assert sorted(ids[0]) == [4, 5]
+
+
+def test_route_k1_weight_is_alpha():
+    rs = np.random.default_rng(5)
+    z = rs.standard_normal((32, 16)).astype(np.float32)
+    _, wts = oracle.route(z, 4, 2, 1, 2.5)
+    assert (wts == np.float32(2.5)).all()
+
+
+def test_route_weights_normalised_and_scaled():
+    w = WORKLOADS["beam_prefill_t4096"]
+    rs = np.random.default_rng(9)
+    z = rs.standard_normal((512, w.E)).astype(np.float32) * 2
+    ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True)
+    assert np.allclose(wts.astype(np.float64).sum(1), 2.5, rtol=1e-6, atol=0)
+    s = np.take_along_axis(d["scores"], ids, 1).astype(np.float64)
+    ref = 2.5 * s / s.sum(1, keepdims=True)
+    assert (np.abs(wts - ref) / ref).max() < 1e-6
+    # the selected experts lie inside the kept groups, 8 distinct ids
+    assert ((ids // (w.E // w.G))[:, :, None] == d["kept_groups"][:, None, :]).any(2).all()
+    assert all(len(set(r)) == w.K for r in ids)
+
+
+# ---------------------------------------------------------------------------
+# expert MLP and combine
+# ---------------------------------------------------------------------------
+def test_expert_impulse_closed_form():
+    """x = c e_h0, Wg = a at (j0,h0), Wu = b at (j0,h0), Wd = d at (m0,j0), zero elsewhere:
+    o[m0] = d * SiLU(a c) * (b c), o = 0 elsewhere.  With a c = ln 3,
+    SiLU(ln 3) = 0.75 ln 3.  Pins the layout (gate rows first, Wd[m, j]) and that the
+    SiLU applies to the gate, not to the up projection."""
+    H, I = 12, 5
+    h0, j0, m0 = 7, 3, 2
+    c, a, b, dd = 2.0, math.log(3.0) / 2.0, -1.5, 0.25
+    x = np.zeros((1, H)); x[0, h0] = c
+    w13 = np.zeros((2 * I, H)); w13[j0, h0] = a; w13[I + j0, h0] = b
+    w2 = np.zeros((H, I)); w2[m0, j0] = dd
+    o = oracle.expert_ffn(x, w13, w2)
+    expect = np.zeros(H); expect[m0] = dd * 0.75 * math.log(3.0) * (b * c)
+    assert np.allclose(o[0], expect, rtol=1e-14, atol=1e-15)
+
+
+def _tiny_bank(rs, E, H, I, same=False):
+    w13 = rs.standard_normal((1 if same else E, 2 * I, H)) / math.sqrt(H)
+    w2 = rs.standard_normal((1 if same else E, H, I)) / math.sqrt(I)
+    if same:
+        w13 = np.repeat(w13, E, 0); w2 = np.repeat(w2, E, 0)
+    return oracle.ExpertBank(w13.astype(np.float32), w2.astype(np.float32), "f32")
+
+
+def test_identical_experts_give_alpha_times_ffn():
+    w = WORKLOADS["tiny_f32"]
+    rs = np.random.default_rng(2)
+    bank = _tiny_bank(rs, w.E, w.H, w.I, same=True)
+    x = rs.standard_normal((16, w.H)).astype(np.float32)
+    wr = rs.standard_normal((w.H, w.E)).astype(np.float32)
+    r = oracle.moe_forward(x, wr, None, bank, w.G, w.Kg, w.K, w.alpha)
+    w13, w2 = bank.expert(0)
+    ref = 2.5 * oracle.expert_ffn(x.astype(np.float64), w13, w2)
+    assert np.allclose(r["y"], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_dense_gate_vector_cross_check():
+    """y[t] = sum over ALL experts e of G[t,e] FFN_e(x_t), with G the sparse gate
+    vector (weights at the chosen ids, 0 elsewhere), computed token by token."""
+    w = WORKLOADS["tiny_f32"]
+    inp = make_inputs(w)
+    bank = oracle.ExpertBank(inp.w13, inp.w2, "f32")
+    x = inp.x
+    r = oracle.moe_forward(x, inp.w_router, None, bank, w.G, w.Kg, w.K, w.alpha)
+    for t in range(0, w.T, 5):
+        gate = np.zeros(w.E)
+        gate[r["ids"][t]] = r["w"][t]
+        acc = np.zeros(w.H)
+        for e in range(w.E):
+            w13, w2 = bank.expert(e)
+            acc += gate[e] * oracle.expert_ffn(x[t:t + 1].astype(np.float64), w13, w2)[0]
+        assert np.allclose(r["y"][t], acc, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_linear_in_down_projection():
+    w = WORKLOADS["tiny_f32"]
+    inp = make_inputs(w)
+    b1 = oracle.ExpertBank(inp.w13, inp.w2, "f32")
+    b2 = oracle.ExpertBank(inp.w13, inp.w2 * 2, "f32")
+    r1 = oracle.moe_forward(inp.x, inp.w_router, None, b1, w.G, w.Kg, w.K, w.alpha)
+    r2 = oracle.moe_forward(inp.x, inp.w_router, None, b2, w.G, w.Kg, w.K, w.alpha)
+    assert np.allclose(r2["y"], 2 * r1["y"], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+def test_e4m3_decode_matches_spec_facts_and_torch():
+    import torch
+    tab = oracle.E4M3_TABLE
+    assert tab[0x7E] == 448.0 and tab[0xFE] == -448.0       # max normal
+    assert tab[0x08] == 2.0 ** -6                             # min normal
+    assert tab[0x01] == 2.0 ** -9                             # min subnormal
+    assert tab[0x38] == 1.0 and tab[0x40] == 2.0 and tab[0x3F] == 1.875
+    assert np.isnan(tab[0x7F]) and np.isnan(tab[0xFF])
+    pos = tab[:0x7F]
+    assert (np.diff(pos) > 0).all()                           # monotone code order
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.nan_to_num(tab, nan=1e9), np.nan_to_num(t, nan=1e9))
+
+
+def test_bf16_widening_matches_torch():
+    import torch
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(mine[fin].view(np.uint32), ref[fin].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# norms and residual
+# ---------------------------------------------------------------------------
+def test_prenorm_closed_forms_and_order():
+    H = 5120
+    c = np.float32(0.75)
+    xh, r = oracle.prenorm(np.full((1, H), c, np.float32), None, 1e-6)
+    assert abs(float(xh[0, 0]) - 0.75 / math.sqrt(0.5625 + 1e-6)) < 2e-7
+    x = normal(0, (77,), (16, H))
+    xh, r = oracle.prenorm(x, None, 1e-6)
+    ms = np.mean(x.astype(np.float64) ** 2, 1)
+    got = np.mean(xh.astype(np.float64) ** 2, 1)
+    assert np.allclose(got, ms / (ms + 1e-6), rtol=1e-5)
+    # exact-rational check of the fixed order on a short row
+    xs = normal(0, (78,), (1, 130))
+    p = [0.0] * 64
+    for l in range(64):
+        for h in range(l, 130, 64):
+            p[l] = fma_f32(xs[0, h], xs[0, h], p[l])
+    o = 32
+    while o >= 1:
+        for l in range(o):
+            p[l] = round_f32(Fraction(p[l]) + Fraction(p[l + o]))
+        o //= 2
+    ms32 = round_f32(Fraction(p[0]) / 130)
+    rr = round_f32(1 / Fraction(math.sqrt(float(np.float32(ms32 + np.float32(1e-6))))))
+    _, r1 = oracle.prenorm(xs, None, 1e-6)
+    # r = 1/sqrtf(ms+eps): sqrt correctly rounded, then a correctly rounded reciprocal
+    s32 = np.sqrt(np.float32(ms32) + np.float32(1e-6), dtype=np.float32)
+    assert r1[0] == np.float32(1.0) / s32
+    assert abs(float(r1[0]) - rr) <= 1e-6 * rr
+
+
+def test_residual_constant_scale_and_equal_weights():
+    """c1^2 + c2^2 = 1; after steps 2..n the stream is (1/sqrt n) * (embedding + sum
+    of outputs): every contribution carries the same weight (pages: 104 additions)."""
+    facts = json.load(open(os.path.join(GOLDEN, "beam_page_facts.json")))
+    for k in range(2, 200):
+        c1, c2 = oracle.residual_coeffs(k)
+        assert abs(c1 * c1 + c2 * c2 - 1.0) < 1e-15
+    n_add = facts["residual_additions"]
+    n = n_add + 1                       # the embedding is step 1
+    dim = n
+    h = np.zeros((1, dim)); h[0, 0] = 1.0          # embedding = unit vector 0
+    for k in range(2, n + 1):
+        out = np.zeros((1, dim)); out[0, k - 1] = 1.0
+        h = oracle.residual_update(h, out, k)
+    assert np.allclose(h, 1 / math.sqrt(n), rtol=1e-12)
+
+
+def test_page_shape_facts():
+    """Param-count identities printed on the pages fix the expert shape."""
+    f = json.load(open(os.path.join(GOLDEN, "beam_page_facts.json")))
+    w = WORKLOADS["beam_prefill_t4096"]
+    assert (w.H, w.I, w.E, w.G, w.Kg, w.K, w.alpha) == (
+        f["hidden_size"], f["expert_intermediate"], f["experts_per_layer"], f["groups"],
+        f["kept_groups"], f["routed_per_token"], f["routed_scale"])
+    assert w.E // w.G == f["group_size"]
+    per_expert = 3 * w.H * w.I
+    assert abs(per_expert / f["params_per_expert"] - 1) < 0.01
+    share = f["moe_layers"] * w.E * per_expert / f["total_params"]
+    assert abs(share - f["expert_param_share"]) < 0.001
+    # active per token = 49 layers x 8 routed experts + the non-expert parameters
+    active = f["moe_layers"] * w.K * per_expert + f["non_expert_params"]
+    assert abs(active / f["active_params"] - 1) < 0.02
