@@ -1,0 +1,200 @@
+"""Benchmark of the Beam MoE layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one full `beam_moe_forward` (router, permutation, gate/up GEMM with SwiGLU,
+down GEMM, combine) -- or `beam_moe_sublayer_forward` for the sublayer workload -- over
+one batch of seeded synthetic Beam-shaped inputs already resident in HBM.  Prints ONE
+JSON line on stdout; progress goes to stderr.
+
+Default workload: the Beam-shaped decode batch (T = 16 tokens, hidden 5120, 256 experts
+in 8 groups of 32, top-4 groups, top-8, SwiGLU intermediate 2560, BF16 experts), where
+the layer streams the weights of every routed expert from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % of MI355X MFMA peak (prefill) / HBM GB/s (decode)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {1: 2500.0, 2: 5000.0, 0: 157.3}     # bf16, fp8, fp32 dense
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="beam_decode_t16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer is built and timed on a single MI355X; "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_mixture_experts_group_amd as bm
+    from beam_inputs import WORKLOADS, make_inputs, DT_BF16, DT_FP8, DT_F32, DTYPE_NAMES
+
+    w = WORKLOADS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    log(f"[bench] generating inputs for {w.name} (T={w.T}) ...")
+    inp = make_inputs(w)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+
+    def up(a, dt=None):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x = up(inp.x)
+    wr = up(inp.w_router)
+    w13, w2 = up(inp.w13), up(inp.w2)
+    s13 = up(inp.w13_scale) if inp.w13_scale is not None else None
+    s2 = up(inp.w2_scale) if inp.w2_scale is not None else None
+    bias = up(inp.logit_bias) if inp.logit_bias is not None else None
+    cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg, topk=w.K,
+                         routed_scale=w.alpha, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
+                         fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+    ws = bm.alloc_workspace(cfg, w.T, dev)
+    ids = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    h = x.clone()      # the sublayer updates the residual stream in place, step after step
+
+    def step():
+        if w.sublayer:
+            bm.beam_moe_sublayer_forward(cfg, h, w.step_k, wr, w13, w2, logit_bias=bias, w13_scale=s13,
+                                         w2_scale=s2, ids=ids, weights=wts, ws=ws)
+        else:
+            bm.beam_moe_forward(cfg, x, wr, w13, w2, logit_bias=bias, w13_scale=s13, w2_scale=s2, y=y, ids=ids,
+                                weights=wts, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    timer = bm.KernelTimer(bm.BEAM_KERNEL_GATE_UP, K)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with timer:
+        ev0.record()
+        for _ in range(K):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_gpu = ev0.elapsed_time(ev1) / K
+    ms_wall = (wall1 - wall0) * 1e3 / K
+    ms_per_step = max(ms_gpu, ms_wall)
+    gate_up_ms = float(np.mean(timer.times_ms()))
+    tokens_per_s = w.T / (ms_per_step / 1e3)
+
+    # ---- roofline of the dominant kernel (grouped gate/up GEMM) ----
+    ids_np = ids.cpu().numpy()
+    n_active = int(np.unique(ids_np).size)
+    P = w.T * w.K
+    wbytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[w.weight_dtype]
+    abytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[w.weight_dtype]
+    gate_up_weight_bytes = n_active * 2 * w.I * w.H * wbytes
+    if w.weight_dtype == DT_FP8:
+        gate_up_weight_bytes += n_active * (2 * w.I // 128) * (w.H // 128) * 4
+    gate_up_bytes = gate_up_weight_bytes + w.T * w.H * abytes + P * w.I * 2
+    gate_up_flops = 2.0 * P * w.H * 2 * w.I
+    peak_tf = MFMA_PEAK_TFLOPS[w.weight_dtype]
+    t_hbm = gate_up_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = gate_up_flops / (peak_tf * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = gate_up_bytes / (gate_up_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = gate_up_flops / (gate_up_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4)}
+    roof.update({"kernel": "grouped gate/up GEMM + SwiGLU", "kernel_ms": round(gate_up_ms, 4),
+                 "algorithmic_bytes": int(gate_up_bytes), "algorithmic_flops": gate_up_flops,
+                 "traffic": None})
+
+    # ---- whole-layer figures ----
+    layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
+    layer_wbytes = n_active * 3 * w.I * w.H * wbytes
+    extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
+             "layer_weight_gbs": round(layer_wbytes / (ms_per_step / 1e3) / 1e9, 1),
+             "distinct_experts": n_active, "ms_gpu_events": round(ms_gpu, 4), "ms_wall": round(ms_wall, 4)}
+
+    # ---- CPU oracle baseline on a bounded sample ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, args.cpu_sample_tokens)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAMES[w.weight_dtype] if w.weight_dtype != DT_F32 else "f32",
+        "data": "synthetic (seeded Philox normals, Beam-shaped, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
+                   "groups": w.G, "topk_groups": w.Kg, "topk": w.K, "routed_scale": w.alpha,
+                   "weights": DTYPE_NAMES[w.weight_dtype], "sublayer": w.sublayer,
+                   "zipf_s": w.zipf_s, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, n_tok):
+    """Time the CPU oracle (as it stands) on the first n_tok tokens of the workload:
+    full FP32 routing of those tokens plus their float64 expert MLPs and combine."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    n = min(n_tok, w.T)
+    if w.act_dtype == 0:
+        x32 = inp.x[:n]
+    else:
+        x32 = oracle.bf16_to_f32(inp.x[:n])
+    bank = oracle.ExpertBank(inp.w13, inp.w2, {0: "f32", 1: "bf16", 2: "fp8_e4m3"}[w.weight_dtype],
+                             inp.w13_scale, inp.w2_scale, w.fp8_block)
+    log(f"[bench] timing the CPU oracle on {n} tokens ...")
+    t0 = time.perf_counter()
+    if w.sublayer:
+        oracle.sublayer_forward(x32, None, None, w.step_k, w.norm_eps, inp.w_router, inp.logit_bias, bank,
+                                w.G, w.Kg, w.K, w.alpha)
+    else:
+        oracle.moe_forward(x32, inp.w_router, inp.logit_bias, bank, w.G, w.Kg, w.K, w.alpha)
+    dt = time.perf_counter() - t0
+    log(f"[bench] CPU oracle: {dt:.2f}s")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(max(oracle.num_threads(), blas)),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n} tokens of {w.name}: FP32 routing + float64 expert MLPs and combine"}
+
+
+if __name__ == "__main__":
+    main()

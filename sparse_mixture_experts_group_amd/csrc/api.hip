@@ -1,0 +1,364 @@
+// C ABI of libbeam_moe: validation, workspace layout and kernel sequencing.
+// The declarations and the full contract of every entry point are in beam_moe.h.
+#include <math.h>
+#include <string.h>
+
+#include "beam_moe.h"
+#include "kernels.h"
+
+using namespace beam;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Structural validity of the configuration (independent of kernel support).
+bool config_valid(const beam_moe_config* c) {
+    if (!c) return false;
+    if (c->hidden < 1 || c->inter < 1) return false;
+    if (c->n_experts < 2 || c->n_experts > kMaxExperts) return false;
+    if (c->n_groups < 1 || c->n_experts % c->n_groups != 0) return false;
+    const int S = c->n_experts / c->n_groups;
+    if (S < 2) return false;
+    if (c->topk_groups < 1 || c->topk_groups > c->n_groups) return false;
+    if (c->topk < 1 || c->topk > kMaxTopK || c->topk > c->topk_groups * S) return false;
+    if (!isfinite(c->routed_scale)) return false;
+    if (c->act_dtype < BEAM_DTYPE_F32 || c->act_dtype > BEAM_DTYPE_FP8_E4M3) return false;
+    if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_FP8_E4M3) return false;
+    if (!(c->norm_eps >= 0.0f) || !isfinite(c->norm_eps)) return false;
+    return true;
+}
+
+// Whether kernels exist for this (valid) configuration.
+bool config_supported(const beam_moe_config* c) {
+    const int a = c->act_dtype, w = c->weight_dtype;
+    const bool pair_ok = (a == BEAM_DTYPE_F32 && w == BEAM_DTYPE_F32) ||
+                         (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_BF16) ||
+                         (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_FP8_E4M3);
+    if (!pair_ok) return false;
+    if (w == BEAM_DTYPE_F32) {
+        if (c->hidden % 64 || c->inter % 64) return false;
+    } else {
+        if (c->hidden % 128 || c->inter % 128) return false;
+    }
+    if (w == BEAM_DTYPE_FP8_E4M3 && c->fp8_block != 128) return false;
+    const int V = scores_per_lane(c->n_experts);
+    const int S = c->n_experts / c->n_groups;
+    if (S % V != 0 || !is_pow2(S / V)) return false;
+    if (c->n_groups > 64) return false;
+    return true;
+}
+
+struct Layout {
+    size_t z, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
+    size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm;
+    size_t total;
+    int nblk, max_tiles;
+};
+
+Layout make_layout(const beam_moe_config& c, int64_t T) {
+    Layout L;
+    const int64_t E = c.n_experts, K = c.topk, H = c.hidden, I = c.inter;
+    const int64_t P = T * K;
+    const bool f32 = c.weight_dtype == BEAM_DTYPE_F32;
+    const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3;
+    const bool bf16_act = c.act_dtype == BEAM_DTYPE_BF16;
+    L.nblk = static_cast<int>((T + kSelectTokens - 1) / kSelectTokens);
+    L.max_tiles = static_cast<int>((P + kPrefillBM - 1) / kPrefillBM + E);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+    L.z = take(sizeof(float) * T * E);
+    L.ids = take(sizeof(int32_t) * P);
+    L.wts = take(sizeof(float) * P);
+    L.blk_cnt = take(sizeof(int32_t) * L.nblk * E);
+    L.blk_off = take(sizeof(int32_t) * L.nblk * E);
+    L.pair_rank = take(sizeof(int32_t) * P);
+    L.exp_cnt = take(sizeof(int32_t) * E);
+    L.exp_off = take(sizeof(int32_t) * (E + 1));
+    L.tiles = take(sizeof(int2) * L.max_tiles);
+    L.meta = take(sizeof(int32_t) * kMetaInts);
+    L.active = take(sizeof(int32_t) * E);
+    L.row_of_pair = take(sizeof(int32_t) * P);
+    L.pair_of_row = take(sizeof(int32_t) * P);
+    // sublayer (BF16 residual stream): FP32 normalised input for the router, and the
+    // expert input in the weights' format
+    L.xhat32 = bf16_act ? take(sizeof(float) * T * H) : off;
+    L.x16 = (bf16_act && !fp8) ? take(sizeof(uint16_t) * T * H) : off;
+    L.x8 = fp8 ? take(T * H) : off;
+    L.x8s = fp8 ? take(sizeof(float) * T) : off;
+    L.hbuf = take((f32 ? 4 : 2) * P * I);
+    L.h8 = fp8 ? take(P * I) : off;
+    L.h8s = fp8 ? take(sizeof(float) * P) : off;
+    L.yperm = take((f32 ? 4 : 2) * P * H);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int check_common(const beam_moe_config* cfg, int64_t T) {
+    if (!config_valid(cfg) || T < 0) return BEAM_ERR_INVALID_ARG;
+    if (T > 0 && T * cfg->topk > INT32_MAX / 2) return BEAM_ERR_INVALID_ARG;
+    if (!config_supported(cfg)) return BEAM_ERR_UNSUPPORTED;
+    return BEAM_OK;
+}
+
+int check_ws(const beam_moe_config* cfg, int64_t T, void* ws, size_t ws_bytes) {
+    const Layout L = make_layout(*cfg, T);
+    if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return BEAM_ERR_INVALID_ARG;
+    return BEAM_OK;
+}
+
+// Kernel timing hook state (see beam_moe_time_kernel).
+struct TimingHook {
+    int kernel = BEAM_KERNEL_NONE;
+    void* const* events = nullptr;
+    int n_pairs = 0;
+    int next = 0;
+};
+TimingHook g_hook;
+
+struct Bracket {
+    hipStream_t st;
+    hipEvent_t stop = nullptr;
+    Bracket(int kernel, hipStream_t s) : st(s) {
+        if (g_hook.kernel == kernel && g_hook.next < g_hook.n_pairs) {
+            const int i = g_hook.next++;
+            (void)hipEventRecord(static_cast<hipEvent_t>(g_hook.events[2 * i]), st);
+            stop = static_cast<hipEvent_t>(g_hook.events[2 * i + 1]);
+        }
+    }
+    ~Bracket() {
+        if (stop) (void)hipEventRecord(stop, st);
+    }
+};
+
+int launch_status() {
+    return hipGetLastError() == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
+}
+
+// Router + permutation.  x_router is FP32 or BF16 [T, H].
+void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
+                const void* x_router, bool x_bf16, const float* w_router, const float* bias,
+                int32_t* ids, float* wts, bool permute) {
+    const int E = c.n_experts, K = c.topk;
+    float* z = at<float>(ws, L.z);
+    {
+        Bracket b(BEAM_KERNEL_ROUTER_LOGITS, st);
+        launch_router_logits(st, static_cast<int>(T), c.hidden, E, x_bf16, x_router, w_router, bias, z);
+    }
+    launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, ids, wts,
+                         at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
+    if (!permute) return;
+    launch_route_scan(st, L.nblk, E, kPrefillBM, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off),
+                      at<int32_t>(ws, L.exp_cnt), at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles),
+                      at<int32_t>(ws, L.meta), at<int32_t>(ws, L.active));
+    launch_route_scatter(st, T * K, K, E, ids, at<int32_t>(ws, L.pair_rank), at<int32_t>(ws, L.blk_off),
+                         at<int32_t>(ws, L.row_of_pair), at<int32_t>(ws, L.pair_of_row));
+}
+
+GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, void* ws) {
+    GroupedGemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.pair_of_row = at<int32_t>(ws, L.pair_of_row);
+    g.topk = c.topk;
+    g.exp_cnt = at<int32_t>(ws, L.exp_cnt);
+    g.exp_off = at<int32_t>(ws, L.exp_off);
+    g.tiles = at<int2>(ws, L.tiles);
+    g.meta = at<int32_t>(ws, L.meta);
+    g.active = at<int32_t>(ws, L.active);
+    g.max_tiles = L.max_tiles;
+    const int64_t P = T * c.topk;
+    g.max_active = static_cast<int>(P < c.n_experts ? P : c.n_experts);
+    return g;
+}
+
+// Expert GEMMs: x_exp [T, H] in the weights' activation format -> yperm [T*K, H].
+void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
+                 const void* x_exp, const float* x_exp_scale, const void* w13,
+                 const float* w13_scale, const void* w2, const float* w2_scale,
+                 const int32_t* ids) {
+    const int64_t P = T * c.topk;
+    const int H = c.hidden, I = c.inter;
+    GroupedGemmArgs g1 = base_args(c, T, L, ws);
+    g1.a = x_exp; g1.lda = H; g1.gather = true; g1.a_scale = x_exp_scale;
+    g1.w = w13; g1.w_scale = w13_scale; g1.n_out = I; g1.kd = H;
+    g1.out = at<void>(ws, L.hbuf); g1.ldo = I;
+    GroupedGemmArgs g2 = base_args(c, T, L, ws);
+    g2.lda = I; g2.gather = false;
+    g2.w = w2; g2.w_scale = w2_scale; g2.n_out = H; g2.kd = I;
+    g2.out = at<void>(ws, L.yperm); g2.ldo = H;
+    const bool decode = T <= kDecodeMaxT;
+    if (c.weight_dtype == BEAM_DTYPE_F32) {
+        { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_f32(st, kGateUp, g1, P, ids); }
+        g2.a = at<void>(ws, L.hbuf);
+        { Bracket b(BEAM_KERNEL_DOWN, st); launch_gemm_f32(st, kDown, g2, P, ids); }
+    } else if (c.weight_dtype == BEAM_DTYPE_BF16) {
+        {
+            Bracket b(BEAM_KERNEL_GATE_UP, st);
+            if (decode) launch_gemm_bf16_decode(st, kGateUp, g1);
+            else launch_gemm_bf16_prefill(st, kGateUp, g1);
+        }
+        g2.a = at<void>(ws, L.hbuf);
+        {
+            Bracket b(BEAM_KERNEL_DOWN, st);
+            if (decode) launch_gemm_bf16_decode(st, kDown, g2);
+            else launch_gemm_bf16_prefill(st, kDown, g2);
+        }
+    } else {
+        { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_fp8(st, kGateUp, g1, decode); }
+        launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
+        g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
+        { Bracket b(BEAM_KERNEL_DOWN, st); launch_gemm_fp8(st, kDown, g2, decode); }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_moe_status_string(int status) {
+    switch (status) {
+        case BEAM_OK: return "BEAM_OK";
+        case BEAM_ERR_INVALID_ARG: return "BEAM_ERR_INVALID_ARG: null pointer, bad shape or bad config";
+        case BEAM_ERR_UNSUPPORTED: return "BEAM_ERR_UNSUPPORTED: no kernels for this configuration";
+        case BEAM_ERR_WORKSPACE: return "BEAM_ERR_WORKSPACE: workspace missing or smaller than beam_moe_workspace_size()";
+        case BEAM_ERR_HIP: return "BEAM_ERR_HIP: a kernel launch failed";
+        default: return "unknown beam_status";
+    }
+}
+
+int beam_moe_abi_version(void) { return BEAM_MOE_ABI_VERSION; }
+
+size_t beam_moe_workspace_size(const beam_moe_config* cfg, int64_t T) {
+    if (!config_valid(cfg) || T < 0) return 0;
+    return make_layout(*cfg, T).total;
+}
+
+int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_map* out) {
+    if (!config_valid(cfg) || T < 0 || !out) return BEAM_ERR_INVALID_ARG;
+    const Layout L = make_layout(*cfg, T);
+    out->logits = L.z;
+    out->expert_count = L.exp_cnt;
+    out->expert_off = L.exp_off;
+    out->row_of_pair = L.row_of_pair;
+    out->pair_of_row = L.pair_of_row;
+    out->hidden = L.hbuf;
+    out->expert_out = L.yperm;
+    out->total = L.total;
+    return BEAM_OK;
+}
+
+int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
+                   const float* logit_bias, int32_t* ids, float* weights, void* ws, size_t ws_bytes,
+                   void* stream) {
+    int s = check_common(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (cfg->act_dtype == BEAM_DTYPE_FP8_E4M3) return BEAM_ERR_UNSUPPORTED;
+    if (T == 0) return BEAM_OK;
+    if (!x || !w_router || !ids || !weights) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return BEAM_ERR_INVALID_ARG;
+    if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = make_layout(*cfg, T);
+    run_router(*cfg, T, L, ws, st, x, cfg->act_dtype == BEAM_DTYPE_BF16, w_router, logit_bias, ids, weights, false);
+    return launch_status();
+}
+
+static int check_weights(const beam_moe_config* cfg, const void* w13, const float* w13_scale, const void* w2,
+                         const float* w2_scale) {
+    if (!w13 || !w2) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(w13) || !aligned16(w2)) return BEAM_ERR_INVALID_ARG;
+    const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3;
+    if (fp8 != (w13_scale != nullptr) || fp8 != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
+    return BEAM_OK;
+}
+
+int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
+                     const float* logit_bias, const void* w13, const float* w13_scale, const void* w2,
+                     const float* w2_scale, void* y, int32_t* ids_out, float* weights_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int s = check_common(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (T == 0) return BEAM_OK;
+    if (!x || !w_router || !y) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y)) return BEAM_ERR_INVALID_ARG;
+    if ((s = check_weights(cfg, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
+    if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = make_layout(*cfg, T);
+    int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
+    float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
+    const bool bf16_act = cfg->act_dtype == BEAM_DTYPE_BF16;
+    run_router(*cfg, T, L, ws, st, x, bf16_act, w_router, logit_bias, ids, wts, true);
+    const void* x_exp = x;
+    const float* x_exp_scale = nullptr;
+    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3) {
+        launch_quant_rows_fp8(st, T, cfg->hidden, true, x, at<uint8_t>(ws, L.x8), at<float>(ws, L.x8s));
+        x_exp = at<void>(ws, L.x8);
+        x_exp_scale = at<float>(ws, L.x8s);
+    }
+    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids);
+    Bracket b(BEAM_KERNEL_COMBINE, st);
+    launch_combine(st, T, cfg->hidden, cfg->topk, cfg->weight_dtype == BEAM_DTYPE_F32, at<void>(ws, L.yperm),
+                   at<int32_t>(ws, L.row_of_pair), wts, y);
+    return launch_status();
+}
+
+int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, const float* pre_gain,
+                              const float* post_gain, int32_t step_k, const float* w_router,
+                              const float* logit_bias, const void* w13, const float* w13_scale,
+                              const void* w2, const float* w2_scale, void* moe_out, int32_t* ids_out,
+                              float* weights_out, void* ws, size_t ws_bytes, void* stream) {
+    int s = check_common(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (cfg->act_dtype != BEAM_DTYPE_BF16) return BEAM_ERR_UNSUPPORTED;
+    if (step_k < 2) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!h || !w_router) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(w_router) || (moe_out && !aligned16(moe_out))) return BEAM_ERR_INVALID_ARG;
+    if ((s = check_weights(cfg, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
+    if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = make_layout(*cfg, T);
+    int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
+    float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
+    const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3;
+    const int H = cfg->hidden;
+    launch_prenorm(st, T, H, static_cast<const uint16_t*>(h), pre_gain, cfg->norm_eps, at<float>(ws, L.xhat32),
+                   fp8 ? nullptr : at<uint16_t>(ws, L.x16), fp8 ? at<uint8_t>(ws, L.x8) : nullptr,
+                   fp8 ? at<float>(ws, L.x8s) : nullptr);
+    run_router(*cfg, T, L, ws, st, at<float>(ws, L.xhat32), false, w_router, logit_bias, ids, wts, true);
+    const void* x_exp = fp8 ? at<void>(ws, L.x8) : at<void>(ws, L.x16);
+    const float* x_exp_scale = fp8 ? at<float>(ws, L.x8s) : nullptr;
+    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids);
+    // c1 = sqrt((k-1)/k), c2 = 1/sqrt(k), each computed in double and rounded once
+    const double k = static_cast<double>(step_k);
+    const float c1 = static_cast<float>(sqrt((k - 1.0) / k));
+    const float c2 = static_cast<float>(1.0 / sqrt(k));
+    Bracket b(BEAM_KERNEL_COMBINE, st);
+    launch_post_residual(st, T, H, cfg->topk, at<uint16_t>(ws, L.yperm), at<int32_t>(ws, L.row_of_pair), wts,
+                         post_gain, cfg->norm_eps, c1, c2, static_cast<uint16_t*>(h),
+                         static_cast<uint16_t*>(moe_out));
+    return launch_status();
+}
+
+int beam_moe_time_kernel(int kernel, void* const* events, int n_pairs) {
+    if (kernel < BEAM_KERNEL_NONE || kernel > BEAM_KERNEL_COMBINE || n_pairs < 0) return BEAM_ERR_INVALID_ARG;
+    if (n_pairs > 0 && !events) return BEAM_ERR_INVALID_ARG;
+    g_hook.kernel = (n_pairs > 0) ? kernel : BEAM_KERNEL_NONE;
+    g_hook.events = events;
+    g_hook.n_pairs = n_pairs;
+    g_hook.next = 0;
+    return BEAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+// Combine, norm, residual and activation-quantisation kernels of libbeam_moe.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace beam {
+
+// ---------------------------------------------------------------------------
+// combine: y[t] = sum_{i=0..K-1} w[t,i] * expert_out[row_of_pair[t*K+i]], i ascending
+// (Reflection Beam 1.0 overview, "Mixture of Experts": expert outputs combined with the
+// normalised router weights, which already carry the factor 2.5).  FP32 accumulation.
+// One block per token; 8 BF16 columns per thread per step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_bf16(int H, int K, const uint16_t* __restrict__ yperm,
+                                                    const int32_t* __restrict__ row_of_pair,
+                                                    const float* __restrict__ w,
+                                                    uint16_t* __restrict__ y) {
+    const int64_t t = blockIdx.x;
+    __shared__ int32_t s_row[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    if (threadIdx.x < K) {
+        s_row[threadIdx.x] = row_of_pair[t * K + threadIdx.x];
+        s_w[threadIdx.x] = w[t * K + threadIdx.x];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < K; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(yperm + static_cast<int64_t>(s_row[i]) * H + c);
+            const float wi = s_w[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] = fmaf(wi, __uint_as_float(v[j] << 16), acc[2 * j]);
+                acc[2 * j + 1] = fmaf(wi, __uint_as_float(v[j] & 0xFFFF0000u), acc[2 * j + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j])) |
+                   (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j + 1])) << 16);
+        *reinterpret_cast<u32x4*>(y + t * H + c) = o;
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_f32(int H, int K, const float* __restrict__ yperm,
+                                                   const int32_t* __restrict__ row_of_pair,
+                                                   const float* __restrict__ w, float* __restrict__ y) {
+    const int64_t t = blockIdx.x;
+    for (int c = threadIdx.x; c < H; c += 256) {
+        float acc = 0.0f;
+        for (int i = 0; i < K; ++i)
+            acc = fmaf(w[t * K + i], yperm[static_cast<int64_t>(row_of_pair[t * K + i]) * H + c], acc);
+        y[t * H + c] = acc;
+    }
+}
+
+void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,
+                    const int32_t* row_of_pair, const float* w, void* y) {
+    if (T == 0) return;
+    if (f32)
+        combine_f32<<<static_cast<unsigned>(T), 256, 0, st>>>(H, K, static_cast<const float*>(yperm), row_of_pair, w,
+                                                              static_cast<float*>(y));
+    else
+        combine_bf16<<<static_cast<unsigned>(T), 256, 0, st>>>(H, K, static_cast<const uint16_t*>(yperm), row_of_pair,
+                                                               w, static_cast<uint16_t*>(y));
+}
+
+// ---------------------------------------------------------------------------
+// pre-norm: xhat = (h * r) * gain, r = 1 / sqrt(mean(h^2) + eps), FP32 (Beam overview,
+// "Residual stream": every sublayer is normalised before and after; norms in FP32).
+// Fixed order (its output feeds the bit-reproducible router): lane l accumulates
+// fma(h, h, .) over h = l, l+64, ... ascending; then p[l] += p[l+o] for o = 32..1.
+// One wavefront per token row.  Optional outputs: FP32 xhat (router input), BF16 xhat,
+// E4M3 xhat with one FP32 scale per row (amax / 448).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float prenorm_value(const uint16_t* row, const float* gain, float r, int c) {
+    float v = __fmul_rn(bf16_bits_to_f32(row[c]), r);
+    if (gain) v = __fmul_rn(v, gain[c]);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint16_t* __restrict__ h,
+                                                    const float* __restrict__ gain, float eps,
+                                                    float* __restrict__ xhat32, uint16_t* __restrict__ x16,
+                                                    uint8_t* __restrict__ x8, float* __restrict__ xs) {
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const uint16_t* row = h + t * H;
+    float p = 0.0f;
+    for (int c = lane; c < H; c += 64) {
+        const float v = bf16_bits_to_f32(row[c]);
+        p = __builtin_fmaf(v, v, p);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) p = __fadd_rn(p, __shfl_xor(p, o, kWave));
+    const float ms = __fdiv_rn(__shfl(p, 0, kWave), static_cast<float>(H));
+    const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, eps)));
+    float am = 0.0f;
+    for (int c = lane; c < H; c += 64) {
+        const float v = prenorm_value(row, gain, r, c);
+        if (xhat32) xhat32[t * H + c] = v;
+        if (x16) x16[t * H + c] = f32_to_bf16_bits(v);
+        am = fmaxf(am, fabsf(v));
+    }
+    if (!x8) return;
+    am = wave_max(am);
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    const float inv = 1.0f / sc;
+    for (int c = lane * 4; c < H; c += 256) {
+        const uint32_t q = f32x4_to_e4m3x4(prenorm_value(row, gain, r, c) * inv, prenorm_value(row, gain, r, c + 1) * inv,
+                                           prenorm_value(row, gain, r, c + 2) * inv,
+                                           prenorm_value(row, gain, r, c + 3) * inv);
+        *reinterpret_cast<uint32_t*>(x8 + t * H + c) = q;
+    }
+    if (lane == 0) xs[t] = sc;
+}
+
+void launch_prenorm(hipStream_t st, int64_t T, int H, const uint16_t* h, const float* gain,
+                    float eps, float* xhat32, uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale) {
+    if (T == 0) return;
+    prenorm_rows<<<static_cast<unsigned>((T + 3) / 4), 256, 0, st>>>(T, H, h, gain, eps, xhat32, x_bf16, x_fp8,
+                                                                     x_scale);
+}
+
+// ---------------------------------------------------------------------------
+// row E4M3 quantisation: q[r, c] = E4M3(v / s), s = amax over row r / 448 (1 for an
+// all-zero row).  One wavefront per row, 8 columns per lane per step.
+// ---------------------------------------------------------------------------
+template <bool SRC_BF16>
+__device__ __forceinline__ void load8(const void* src, int64_t i, float* v) {
+    if (SRC_BF16) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(u[j] << 16);
+            v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+template <bool SRC_BF16>
+__global__ __launch_bounds__(256) void quant_rows_fp8(int64_t rows, int cols, const void* __restrict__ src,
+                                                      uint8_t* __restrict__ q, float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int64_t base = r * cols;
+    float am = 0.0f;
+    for (int c = lane * 8; c < cols; c += 512) {
+        float v[8];
+        load8<SRC_BF16>(src, base + c, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    }
+    am = wave_max(am);
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    const float inv = 1.0f / sc;
+    for (int c = lane * 8; c < cols; c += 512) {
+        float v[8];
+        load8<SRC_BF16>(src, base + c, v);
+        u32x2 o;
+        o[0] = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        o[1] = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        *reinterpret_cast<u32x2*>(q + base + c) = o;
+    }
+    if (lane == 0) scale[r] = sc;
+}
+
+void launch_quant_rows_fp8(hipStream_t st, int64_t rows, int cols, bool src_bf16,
+                           const void* src, uint8_t* q, float* scale) {
+    if (rows == 0) return;
+    const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
+    if (src_bf16) quant_rows_fp8<true><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+    else quant_rows_fp8<false><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+}
+
+// ---------------------------------------------------------------------------
+// combine + post-norm + constant-scale residual, one block per token (Beam overview,
+// "Residual stream": at step k the stream keeps sqrt((k-1)/k) of itself and adds
+// 1/sqrt(k) of the normalised sublayer output).  y stays in FP32 registers-by-LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void post_residual(int H, int K, const uint16_t* __restrict__ yperm,
+                                                     const int32_t* __restrict__ row_of_pair,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ gain, float eps,
+                                                     float c1, float c2, uint16_t* __restrict__ h,
+                                                     uint16_t* __restrict__ moe_out) {
+    extern __shared__ float s_y[];            // H floats
+    __shared__ int32_t s_row[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    __shared__ float s_red[4];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < K) {
+        s_row[threadIdx.x] = row_of_pair[t * K + threadIdx.x];
+        s_w[threadIdx.x] = w[t * K + threadIdx.x];
+    }
+    __syncthreads();
+    float ss = 0.0f;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < K; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(yperm + static_cast<int64_t>(s_row[i]) * H + c);
+            const float wi = s_w[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] = fmaf(wi, __uint_as_float(v[j] << 16), acc[2 * j]);
+                acc[2 * j + 1] = fmaf(wi, __uint_as_float(v[j] & 0xFFFF0000u), acc[2 * j + 1]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s_y[c + j] = acc[j];
+            ss = fmaf(acc[j], acc[j], ss);
+        }
+        if (moe_out) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j])) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j + 1])) << 16);
+            *reinterpret_cast<u32x4*>(moe_out + t * H + c) = o;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+    for (int c = threadIdx.x; c < H; c += 256) {
+        float yn = s_y[c] * r;
+        if (gain) yn *= gain[c];
+        const float hv = bf16_bits_to_f32(h[t * H + c]);
+        h[t * H + c] = f32_to_bf16_bits(c1 * hv + c2 * yn);
+    }
+}
+
+void launch_post_residual(hipStream_t st, int64_t T, int H, int K, const uint16_t* yperm,
+                          const int32_t* row_of_pair, const float* w, const float* gain,
+                          float eps, float c1, float c2, uint16_t* h, uint16_t* moe_out) {
+    if (T == 0) return;
+    post_residual<<<static_cast<unsigned>(T), 256, sizeof(float) * H, st>>>(H, K, yperm, row_of_pair, w, gain, eps,
+                                                                             c1, c2, h, moe_out);
+}
+
+}  // namespace beam

@@ -1,0 +1,78 @@
+// Internal launcher interface of libbeam_moe (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+constexpr int kSelectTokens = 32;   // tokens per selection block
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 256;
+constexpr int kMetaTiles = 0;       // meta[0]: number of (expert, row-tile) tiles
+constexpr int kMetaActive = 1;      // meta[1]: number of experts with >= 1 row
+constexpr int kMetaInts = 64;
+
+constexpr int kPrefillBM = 128;     // rows per tile of the prefill grouped GEMMs
+constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
+
+inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
+
+enum GemmMode { kGateUp = 0, kDown = 1 };
+
+// router.hip
+void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
+                          const float* wr, const float* bias, float* z);
+void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
+                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt,
+                          int32_t* pair_rank);
+void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
+                       int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
+                       int32_t* meta, int32_t* active);
+void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const int32_t* ids,
+                          const int32_t* pair_rank, const int32_t* blk_off,
+                          int32_t* row_of_pair, int32_t* pair_of_row);
+
+// Arguments shared by the grouped GEMM launchers.
+struct GroupedGemmArgs {
+    const void* a;            // activations: x [T, Kd] (gathered by token) or h [rows, Kd]
+    int64_t lda;              // elements per activation row
+    bool gather;              // true: row r reads activation row pair_of_row[r] / topk
+    const int32_t* pair_of_row;
+    int topk;
+    const float* a_scale;     // FP8: [rows or T, Kd/128] activation scales, else null
+    const void* w;            // [E, Nw, Kd] expert weights
+    const float* w_scale;     // FP8: [E, Nw/128, Kd/128], else null
+    int n_out;                // output columns (I for gate/up, H for down)
+    int kd;                   // reduction length
+    const int32_t* exp_cnt;   // [E]
+    const int32_t* exp_off;   // [E+1]
+    const int2* tiles;        // [max_tiles] (expert, first row within expert)
+    const int32_t* meta;      // meta[kMetaTiles], meta[kMetaActive]
+    const int32_t* active;    // [E] experts with rows, ascending
+    int max_tiles;            // grid bound for tile-driven kernels
+    int max_active;           // grid bound for expert-driven kernels
+    void* out;                // [rows, n_out]
+    int64_t ldo;              // elements per output row
+};
+
+// gemm_f32.hip (plain FP32, one thread per output)
+void launch_gemm_f32(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int64_t rows,
+                     const int32_t* ids);
+// gemm_bf16.hip
+void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+void launch_gemm_bf16_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// gemm_fp8.hip
+void launch_gemm_fp8(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool decode);
+
+// elementwise.hip
+void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,
+                    const int32_t* row_of_pair, const float* w, void* y);
+void launch_prenorm(hipStream_t st, int64_t T, int H, const uint16_t* h, const float* gain,
+                    float eps, float* xhat32, uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale);
+void launch_quant_rows_fp8(hipStream_t st, int64_t rows, int cols, bool src_bf16,
+                           const void* src, uint8_t* q, float* scale);
+void launch_post_residual(hipStream_t st, int64_t T, int H, int K, const uint16_t* yperm,
+                          const int32_t* row_of_pair, const float* w, const float* gain,
+                          float eps, float c1, float c2, uint16_t* h, uint16_t* moe_out);
+
+}  // namespace beam

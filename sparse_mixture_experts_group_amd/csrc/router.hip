@@ -1,0 +1,363 @@
+// Router and token permutation kernels of libbeam_moe.
+//
+// Router (Reflection Beam 1.0 overview, section "Mixture of Experts: 256 experts,
+// 8 routed per token"): sigmoid scores of all experts, groups of E/G contiguous experts
+// ranked by the sum of their two largest scores, top-Kg groups kept, top-K experts
+// picked inside them, weights = scores normalised over the K picks times alpha.  The
+// router runs in FP32 (same page, section "Residual stream ...", last paragraph).
+//
+// Bit-reproducibility: each logit is one fused multiply-add chain over h ascending
+// (no split of the reduction), the sigmoid uses router_exp and IEEE-rounded division,
+// and every ranking is (value desc, index asc), so expert ids are a pure function of
+// the input bits.  Contraction is disabled in this file so that no a*b+c is fused
+// behind our back.
+#pragma clang fp contract(off)
+
+#include "common.cuh"
+#include "kernels.h"
+
+namespace beam {
+
+// ---------------------------------------------------------------------------
+// logits z[t,e] = fma-chain_h x[t,h] * wr[h,e] (+ bias[e])
+// ---------------------------------------------------------------------------
+template <bool XBF16>
+__device__ __forceinline__ float load_act(const void* x, int64_t i) {
+    if constexpr (XBF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+    else return static_cast<const float*>(x)[i];
+}
+
+// One thread per (t, e): for small T, where a tiled kernel would not fill the chip.
+template <bool XBF16>
+__global__ __launch_bounds__(64) void router_logits_simple(int T, int H, int E, const void* x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ z) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<int64_t>(T) * E) return;
+    const int t = static_cast<int>(idx / E);
+    const int e = static_cast<int>(idx % E);
+    const int64_t xrow = static_cast<int64_t>(t) * H;
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int h = 0; h < H; ++h)
+        acc = __builtin_fmaf(load_act<XBF16>(x, xrow + h), wr[static_cast<int64_t>(h) * E + e], acc);
+    if (bias) acc = __fadd_rn(acc, bias[e]);
+    z[idx] = acc;
+}
+
+// Register-tiled version: block = BT tokens x BE experts, 256 threads as 16 x 16, each
+// thread owns a (BT/16) x (BE/16) accumulator tile and walks h in ascending order, so
+// every accumulator is still a single ascending fma chain.  Tiles of HK hidden
+// entries are staged through LDS (x transposed so a thread's tokens are contiguous).
+template <bool XBF16, int BT, int BE>
+__global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, const void* x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ z) {
+    constexpr int HK = 32;
+    constexpr int TM = BT / 16, TN = BE / 16;
+    constexpr int XP = BT + 4;               // padded LDS pitch of the transposed x tile
+    __shared__ float xs[HK * XP];
+    __shared__ float ws[HK * BE];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+
+    // x tile: BT rows x HK cols = BT*HK/256 elements per thread (contiguous in h)
+    constexpr int XE = BT * HK / 256;         // 8 for BT=64, 4 for BT=32
+    const int xr = tid / (HK / XE), xc = (tid % (HK / XE)) * XE;
+    const int xt = min(t0 + xr, T - 1);
+    // w tile: HK rows x BE cols, float4 chunks
+    constexpr int WV = HK * BE / 4 / 256;
+
+    for (int h0 = 0; h0 < H; h0 += HK) {
+        float xv[XE];
+#pragma unroll
+        for (int i = 0; i < XE; ++i) xv[i] = load_act<XBF16>(x, static_cast<int64_t>(xt) * H + h0 + xc + i);
+        float4 wv[WV];
+#pragma unroll
+        for (int i = 0; i < WV; ++i) {
+            const int c = tid + i * 256;
+            const int k = c / (BE / 4), cc = (c % (BE / 4)) * 4;
+            wv[i] = *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(h0 + k) * E + e0 + cc);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < XE; ++i) xs[(xc + i) * XP + xr] = xv[i];
+#pragma unroll
+        for (int i = 0; i < WV; ++i) {
+            const int c = tid + i * 256;
+            const int k = c / (BE / 4), cc = (c % (BE / 4)) * 4;
+            *reinterpret_cast<float4*>(&ws[k * BE + cc]) = wv[i];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < HK; ++k) {
+            float a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = xs[k * XP + ty * TM + i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[j] = ws[k * BE + tx * TN + j];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int t = t0 + ty * TM + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int e = e0 + tx * TN + j;
+            float v = acc[i][j];
+            if (bias) v = __fadd_rn(v, bias[e]);
+            z[static_cast<int64_t>(t) * E + e] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// selection: one wavefront per token
+// ---------------------------------------------------------------------------
+// Lane l holds the V scores of experts l*V .. l*V+V-1.  A group of S experts spans
+// L = S/V lanes (a power of two), so the group's top-2 pair is reduced with xor
+// shuffles inside aligned lane segments.  Each "pick the best" round is a wave-wide
+// max followed by a ballot of the lanes holding it; the lowest such lane holds the
+// lowest index with that value (lanes are in index order, and a lane's local best is
+// its first maximum).  The block also records, for the stable token -> expert
+// permutation, how many of its pairs go to each expert and each pair's rank among the
+// block's pairs with the same expert.
+template <int V>
+__global__ __launch_bounds__(256) void router_select(int T, int E, int G, int Kg, int K,
+                                                     float alpha, const float* __restrict__ z,
+                                                     int32_t* __restrict__ ids,
+                                                     float* __restrict__ wts,
+                                                     int32_t* __restrict__ blk_cnt,
+                                                     int32_t* __restrict__ pair_rank) {
+    __shared__ int32_t s_ids[kSelectTokens * kMaxTopK];
+    __shared__ int32_t s_cnt[kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * kSelectTokens;
+    for (int i = threadIdx.x; i < E; i += 256) s_cnt[i] = 0;
+
+    const int S = E / G;
+    const int L = S / V;
+    const int group = (lane * V) / S;
+    const bool lane_live = lane * V < E;
+
+    for (int tl = wave; tl < kSelectTokens; tl += 4) {
+        const int t = t0 + tl;
+        if (t >= T) break;
+        float s[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int e = lane * V + v;
+            s[v] = (e < E) ? router_sigmoid(z[static_cast<int64_t>(t) * E + e]) : -1.0f;
+        }
+        // group top-2 (multiset: a repeated maximum counts twice)
+        float a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (lane * V + v >= E) continue;
+            if (s[v] > a1) { a2 = a1; a1 = s[v]; }
+            else if (s[v] > a2) a2 = s[v];
+        }
+        for (int o = 1; o < L; o <<= 1) {
+            const float b1 = __shfl_xor(a1, o, kWave), b2 = __shfl_xor(a2, o, kWave);
+            const float n1 = fmaxf(a1, b1);
+            const float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+            a1 = n1; a2 = n2;
+        }
+        const bool leader = lane_live && (lane % L == 0);
+        float gv = leader ? __fadd_rn(a1, a2) : -INFINITY;
+
+        // keep Kg groups
+        uint64_t kept = 0;
+        for (int r = 0; r < Kg; ++r) {
+            const float m = wave_max(gv);
+            const int wl = first_lane(wave_ballot(leader && gv == m));
+            kept |= 1ull << ((wl * V) / S);
+            if (lane == wl) gv = -INFINITY;
+        }
+        // candidates: experts inside kept groups only
+        const bool gk = lane_live && ((kept >> group) & 1ull);
+        float c[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) c[v] = (gk && lane * V + v < E) ? s[v] : -1.0f;
+
+        int my_id = 0;
+        float my_s = 0.0f;
+        for (int i = 0; i < K; ++i) {
+            float lb = c[0];
+            int lv = 0;
+#pragma unroll
+            for (int v = 1; v < V; ++v)
+                if (c[v] > lb) { lb = c[v]; lv = v; }
+            const float m = wave_max(lb);
+            const int wl = first_lane(wave_ballot(lb == m));
+            const int wv = __shfl(lv, wl, kWave);
+            if (lane == wl) {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    if (v == lv) c[v] = -1.0f;
+            }
+            if (lane == i) { my_id = wl * V + wv; my_s = m; }
+        }
+        float d = 0.0f;
+        for (int i = 0; i < K; ++i) d = __fadd_rn(d, __shfl(my_s, i, kWave));
+        if (lane < K) {
+            const int64_t p = static_cast<int64_t>(t) * K + lane;
+            ids[p] = my_id;
+            wts[p] = __fmul_rn(__fdiv_rn(my_s, d), alpha);
+            s_ids[tl * K + lane] = my_id;
+        }
+    }
+    __syncthreads();
+    const int ntok = min(kSelectTokens, T - t0);
+    const int np = ntok * K;
+    for (int p = threadIdx.x; p < np; p += 256) {
+        const int e = s_ids[p];
+        int r = 0;
+        for (int q = 0; q < p; ++q) r += (s_ids[q] == e);
+        pair_rank[static_cast<int64_t>(t0) * K + p] = r;
+        atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += 256) blk_cnt[static_cast<int64_t>(blockIdx.x) * E + i] = s_cnt[i];
+}
+
+// ---------------------------------------------------------------------------
+// permutation: per-expert counts, offsets, tile list, active-expert list
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
+    const int tid = threadIdx.x;
+    sh[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int add = tid >= o ? sh[tid - o] : 0;
+        __syncthreads();
+        sh[tid] += add;
+        __syncthreads();
+    }
+    const int incl = sh[tid];
+    total = sh[255];
+    __syncthreads();
+    return incl - v;
+}
+
+// One block of 256 threads; thread e owns expert e (E <= 256).
+__global__ __launch_bounds__(256) void route_scan(int nblk, int E, int BM,
+                                                  const int32_t* __restrict__ blk_cnt,
+                                                  int32_t* __restrict__ blk_off,
+                                                  int32_t* __restrict__ exp_cnt,
+                                                  int32_t* __restrict__ exp_off,
+                                                  int2* __restrict__ tiles,
+                                                  int32_t* __restrict__ meta,
+                                                  int32_t* __restrict__ active) {
+    __shared__ int sh[256];
+    const int e = threadIdx.x;
+    int tot = 0;
+    if (e < E)
+        for (int b = 0; b < nblk; ++b) tot += blk_cnt[static_cast<int64_t>(b) * E + e];
+    int total_rows;
+    const int base = block_exclusive_scan(tot, sh, total_rows);
+    if (e < E) {
+        exp_cnt[e] = tot;
+        exp_off[e] = base;
+        int run = base;
+        for (int b = 0; b < nblk; ++b) {
+            const int64_t i = static_cast<int64_t>(b) * E + e;
+            blk_off[i] = run;
+            run += blk_cnt[i];
+        }
+    }
+    if (e == 0) exp_off[E] = total_rows;
+    const int nt = (e < E) ? (tot + BM - 1) / BM : 0;
+    int total_tiles;
+    const int tbase = block_exclusive_scan(nt, sh, total_tiles);
+    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j * BM);
+    int n_active;
+    const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
+    if (e < E && tot > 0) active[abase] = e;
+    if (e == 0) {
+        meta[kMetaTiles] = total_tiles;
+        meta[kMetaActive] = n_active;
+    }
+}
+
+// pair p = t*K + i -> row = offset of (its select block, its expert) + its rank.
+__global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int E,
+                                                     const int32_t* __restrict__ ids,
+                                                     const int32_t* __restrict__ pair_rank,
+                                                     const int32_t* __restrict__ blk_off,
+                                                     int32_t* __restrict__ row_of_pair,
+                                                     int32_t* __restrict__ pair_of_row) {
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (p >= npairs) return;
+    const int64_t t = p / K;
+    const int64_t b = t / kSelectTokens;
+    const int e = ids[p];
+    const int row = blk_off[b * E + e] + pair_rank[p];
+    row_of_pair[p] = row;
+    pair_of_row[row] = static_cast<int32_t>(p);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
+                          const float* wr, const float* bias, float* z) {
+    // The tiled kernel needs E % 128 == 0 and H % 32 == 0; it pays off once there
+    // are enough token tiles to fill the chip.
+    const bool tiled = (E % 128 == 0) && (H % 32 == 0) && T >= 256;
+    if (!tiled) {
+        const int64_t n = static_cast<int64_t>(T) * E;
+        const int blocks = static_cast<int>((n + 63) / 64);
+        if (x_bf16) router_logits_simple<true><<<blocks, 64, 0, st>>>(T, H, E, x, wr, bias, z);
+        else router_logits_simple<false><<<blocks, 64, 0, st>>>(T, H, E, x, wr, bias, z);
+        return;
+    }
+    if (T >= 16384) {
+        dim3 grid((T + 63) / 64, E / 128);
+        if (x_bf16) router_logits_tiled<true, 64, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        else router_logits_tiled<false, 64, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+    } else {
+        dim3 grid((T + 31) / 32, E / 128);
+        if (x_bf16) router_logits_tiled<true, 32, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        else router_logits_tiled<false, 32, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+    }
+}
+
+void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
+                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt,
+                          int32_t* pair_rank) {
+    const int nblk = (T + kSelectTokens - 1) / kSelectTokens;
+    const int V = scores_per_lane(E);
+    if (V == 1) router_select<1><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+    else if (V == 2) router_select<2><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+    else router_select<4><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+}
+
+void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
+                       int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
+                       int32_t* meta, int32_t* active) {
+    route_scan<<<1, 256, 0, st>>>(nblk, E, BM, blk_cnt, blk_off, exp_cnt, exp_off, tiles, meta, active);
+}
+
+void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const int32_t* ids,
+                          const int32_t* pair_rank, const int32_t* blk_off,
+                          int32_t* row_of_pair, int32_t* pair_of_row) {
+    const int blocks = static_cast<int>((npairs + 255) / 256);
+    route_scatter<<<blocks, 256, 0, st>>>(npairs, K, E, ids, pair_rank, blk_off, row_of_pair, pair_of_row);
+}
+
+}  // namespace beam

@@ -1,0 +1,112 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_group_amd as bm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "beam_moe.h")
+FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(bm.C_FUNCTIONS)
+    L = bm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert bm.abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert bm.status_string(s).startswith("BEAM_")
+    assert "unknown" in bm.status_string(99)
+
+
+def beam(**kw):
+    return bm.make_config(**kw)
+
+
+def test_workspace_size_and_map():
+    c = beam()
+    n16 = bm.beam_moe_workspace_size(c, 16)
+    n4k = bm.beam_moe_workspace_size(c, 4096)
+    assert 0 < n16 < n4k
+    m = bm.beam_moe_workspace_map(c, 4096)
+    assert m["total"] == n4k
+    offs = [m[k] for k in ("logits", "expert_count", "expert_off", "row_of_pair", "pair_of_row", "hidden",
+                           "expert_out")]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    # expert outputs [T*K, H] BF16 are the largest region
+    assert n4k - m["expert_out"] >= 4096 * 8 * 5120 * 2
+    assert bm.beam_moe_workspace_size(c, -1) == 0
+    assert bm.beam_moe_workspace_size(beam(n_groups=3), 16) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(n_groups=3), dict(n_groups=256), dict(topk_groups=9), dict(topk=0),
+                                dict(topk=33), dict(topk_groups=1, topk=33), dict(n_experts=512),
+                                dict(n_experts=1), dict(hidden=0), dict(routed_scale=float("nan")),
+                                dict(act_dtype=7)])
+def test_invalid_config_rejected(kw):
+    c = beam(**kw)
+    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                                   None, FAKE, 1 << 40, None)
+    assert st == bm.BEAM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_BF16),
+                                dict(hidden=5000), dict(inter=100), dict(n_experts=96, n_groups=32),
+                                dict(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3, fp8_block=64)])
+def test_unsupported_config(kw):
+    c = beam(**kw)
+    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                                   None, FAKE, 1 << 40, None)
+    assert st == bm.BEAM_ERR_UNSUPPORTED
+
+
+def test_argument_errors_before_any_launch():
+    c = beam()
+    L = bm.lib()
+    fwd = lambda T, x, y, ws, nb, w13=FAKE, s13=None: L.beam_moe_forward(
+        ctypes.byref(c), T, x, FAKE, None, w13, s13, FAKE, None, y, None, None, ws, nb, None)
+    assert fwd(0, None, None, None, 0) == bm.BEAM_OK                   # T = 0: no-op
+    assert fwd(-1, FAKE, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, None, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, None, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, FAKE, FAKE, 1 << 40, w13=None) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, FAKE, FAKE, 1 << 40, s13=FAKE) == bm.BEAM_ERR_INVALID_ARG   # scale with BF16
+    assert fwd(16, ctypes.c_void_p(0x10008), FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG  # misaligned
+    need = bm.beam_moe_workspace_size(c, 16)
+    assert fwd(16, FAKE, FAKE, FAKE, need - 1) == bm.BEAM_ERR_WORKSPACE
+    assert fwd(16, FAKE, FAKE, None, need) == bm.BEAM_ERR_WORKSPACE
+    # FP8 weights need both scale arrays
+    c8 = beam(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3)
+    st = L.beam_moe_forward(ctypes.byref(c8), 16, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None, None,
+                            FAKE, 1 << 40, None)
+    assert st == bm.BEAM_ERR_INVALID_ARG
+
+
+def test_route_and_sublayer_argument_errors():
+    c = beam()
+    L = bm.lib()
+    assert L.beam_moe_route(ctypes.byref(c), 16, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 40,
+                            None) == bm.BEAM_ERR_INVALID_ARG
+    assert L.beam_moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, 0, None) == bm.BEAM_OK
+    sub = lambda cfg, k, ws_bytes: L.beam_moe_sublayer_forward(
+        ctypes.byref(cfg), 16, FAKE, None, None, k, FAKE, None, FAKE, None, FAKE, None, None, None, None, FAKE,
+        ws_bytes, None)
+    assert sub(c, 1, 1 << 40) == bm.BEAM_ERR_INVALID_ARG                 # step k must be >= 2
+    assert sub(beam(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_F32), 10,
+               1 << 40) == bm.BEAM_ERR_UNSUPPORTED
+    assert sub(c, 10, 16) == bm.BEAM_ERR_WORKSPACE

@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
+inputs.  Routing ids and the permutation are compared bit for bit, FP32 weights within
+1e-6 relative, layer outputs within the stated relative max-norm tolerance
+(||y - y_ref||_inf / ||y_ref||_inf): 1e-5 FP32 layer, 2e-2 BF16 experts, 6e-2 FP8 experts.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_group_amd as bm
+from beam_inputs import DT_BF16, DT_F32, DT_FP8, DTYPE_NAMES, WORKLOADS
+from conftest import gpu_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {DT_F32: 1e-5, DT_BF16: 2e-2, DT_FP8: 6e-2}
+
+
+def cfg_of(w):
+    return bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg, topk=w.K,
+                          routed_scale=w.alpha, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
+                          fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+
+
+def to_dev_x(w, x):
+    if w.act_dtype == DT_F32:
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def x_f32(w, x):
+    return x if w.act_dtype == DT_F32 else oracle.bf16_to_f32(x)
+
+
+def bank_of(w, full):
+    return oracle.ExpertBank(full.w13, full.w2, DTYPE_NAMES[w.weight_dtype], full.w13_scale, full.w2_scale,
+                             w.fp8_block)
+
+
+def dev_bias(bias):
+    return None if bias is None else torch.from_numpy(bias).cuda()
+
+
+def rel_inf(got, ref):
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+def sample_tokens(T, n=16, seed=1):
+    rs = np.random.default_rng(seed)
+    base = {0, T - 1, T // 2}
+    extra = rs.choice(T, size=min(T, n), replace=False)
+    return np.array(sorted(base | set(int(t) for t in extra)))[:max(n, 3)]
+
+
+def run_forward(w, dev, x, bias):
+    cfg = cfg_of(w)
+    xd = to_dev_x(w, x)
+    ids = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    ws = bm.alloc_workspace(cfg, w.T)
+    y = bm.beam_moe_forward(cfg, xd, dev["w_router"], dev["w13"], dev["w2"], logit_bias=dev_bias(bias),
+                            w13_scale=dev.get("w13_scale"), w2_scale=dev.get("w2_scale"), ids=ids, weights=wts,
+                            ws=ws)
+    torch.cuda.synchronize()
+    return cfg, y, ids.cpu().numpy(), wts.cpu().numpy(), ws
+
+
+def ws_region(ws, off, count, dtype):
+    nbytes = count * np.dtype(dtype).itemsize
+    return ws[off:off + nbytes].cpu().numpy().view(dtype)
+
+
+def check_routing(w, ids, wts, ref_ids, ref_w):
+    mism = int((ids != ref_ids).any(axis=1).sum())
+    assert mism == 0, f"{mism} tokens with different expert ids"
+    rel = np.abs(wts.astype(np.float64) - ref_w) / np.abs(ref_w)
+    assert rel.max() <= 1e-6, rel.max()
+
+
+def check_permutation(w, ws, ids):
+    m = bm.beam_moe_workspace_map(cfg_of(w), w.T)
+    P = w.T * w.K
+    cnt = ws_region(ws, m["expert_count"], w.E, np.int32)
+    off = ws_region(ws, m["expert_off"], w.E + 1, np.int32)
+    rop = ws_region(ws, m["row_of_pair"], P, np.int32)
+    por = ws_region(ws, m["pair_of_row"], P, np.int32)
+    flat = ids.reshape(-1)
+    assert np.array_equal(cnt, np.bincount(flat, minlength=w.E))
+    assert off[0] == 0 and np.array_equal(np.diff(off), cnt)
+    # stable order: rows of each expert consecutive, pairs ascending inside an expert
+    assert np.array_equal(por, np.argsort(flat, kind="stable"))
+    assert np.array_equal(rop[por], np.arange(P))
+
+
+# ---------------------------------------------------------------------------
+# tiny FP32 layer: everything checked, every token
+# ---------------------------------------------------------------------------
+def test_tiny_layer_full_parity():
+    w, full, dev, x, bias = gpu_inputs("tiny_f32")
+    print(f"[case] tiny_f32 T={w.T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, bias)
+    ref = oracle.moe_forward(x_f32(w, x), full.w_router, bias, bank_of(w, full), w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, ref["ids"], ref["w"])
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    z = ws_region(ws, m["logits"], w.T * w.E, np.float32).reshape(w.T, w.E)
+    assert np.array_equal(z, ref["logits"])            # logits bit for bit
+    check_permutation(w, ws, ids)
+    assert rel_inf(y.cpu().numpy().astype(np.float64), ref["y"]) <= TOL[DT_F32]
+
+
+@pytest.mark.parametrize("T", [1, 5, 33, 100])
+def test_tiny_layer_ragged_T(T):
+    w, full, dev, x, bias = gpu_inputs("tiny_f32", T)
+    print(f"[case] tiny_f32 T={T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, bias)
+    ref = oracle.moe_forward(x_f32(w, x), full.w_router, bias, bank_of(w, full), w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, ref["ids"], ref["w"])
+    check_permutation(w, ws, ids)
+    assert rel_inf(y.cpu().numpy().astype(np.float64), ref["y"]) <= TOL[DT_F32]
+
+
+def test_router_all_ties_and_duplicated_columns():
+    """W_r = 0: every score ties (ids 0..K-1, weights alpha/K).  Duplicated W_r columns
+    across groups: exact equal scores across groups resolved toward lower indices."""
+    w, full, dev, x, bias = gpu_inputs("beam_decode_t16")
+    print("[case] router ties", flush=True)
+    cfg = cfg_of(w)
+    xd = to_dev_x(w, x)
+    zero = torch.zeros_like(dev["w_router"])
+    ids, wts = bm.beam_moe_route(cfg, xd, zero)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == np.arange(w.K)).all()
+    assert (wts.cpu().numpy() == np.float32(w.alpha / w.K)).all()
+    wr = full.w_router.copy()
+    S = w.E // w.G
+    for g in range(1, w.G):
+        wr[:, g * S:(g + 1) * S] = wr[:, 0:S]          # every group a copy of group 0
+    ids, wts = bm.beam_moe_route(cfg, xd, torch.from_numpy(wr).cuda())
+    torch.cuda.synchronize()
+    z = oracle.router_logits(x_f32(w, x), wr)
+    rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+    assert (ids.cpu().numpy() < w.Kg * S).all()        # equal groups -> the lowest Kg groups
+
+
+# ---------------------------------------------------------------------------
+# Beam-shaped BF16 layer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T", [("beam_decode_t16", None), ("beam_decode_t16", 1),
+                                    ("beam_decode_t16", 17), ("beam_prefill_t4096", None),
+                                    ("beam_prefill_t4096", 4097), ("beam_skewed_t32768", None)])
+def test_beam_bf16_layer(name, T):
+    w, full, dev, x, bias = gpu_inputs(name, T)
+    print(f"[case] {name} T={w.T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, bias)
+    # routing of every token, bit for bit
+    x32 = x_f32(w, x)
+    z = oracle.router_logits(x32, full.w_router, bias)
+    rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, rid, rw)
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    zg = ws_region(ws, m["logits"], w.T * w.E, np.float32).reshape(w.T, w.E)
+    assert np.array_equal(zg, z)
+    check_permutation(w, ws, ids)
+    # layer output on sampled tokens (all tokens for the decode batch)
+    tok = np.arange(w.T) if w.T <= 32 else sample_tokens(w.T)
+    yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
+    yg = y.float().cpu().numpy()[tok].astype(np.float64)
+    err = rel_inf(yg, yref)
+    print(f"[case] {name} T={w.T} rel_inf={err:.3e}", flush=True)
+    assert err <= TOL[w.weight_dtype]
+
+
+def test_beam_bf16_intermediates_and_determinism():
+    """SwiGLU activations (hidden) of sampled rows against the oracle's, and two runs
+    giving bit-identical outputs."""
+    w, full, dev, x, bias = gpu_inputs("beam_prefill_t4096")
+    print("[case] intermediates T=4096", flush=True)
+    cfg, y1, ids, wts, ws = run_forward(w, dev, x, bias)
+    _, y2, _, _, _ = run_forward(w, dev, x, bias)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    P = w.T * w.K
+    por = ws_region(ws, m["pair_of_row"], P, np.int32)
+    hid = ws_region(ws, m["hidden"], P * w.I, np.uint16).reshape(P, w.I)
+    rows = np.random.default_rng(3).choice(P, 24, replace=False)
+    x32 = x_f32(w, x).astype(np.float64)
+    bank = bank_of(w, full)
+    errs = []
+    for r in rows:
+        p = int(por[r]); t, i = divmod(p, w.K)
+        w13, _ = bank.expert(int(ids[t, i]))
+        g = w13[:w.I] @ x32[t]; u = w13[w.I:] @ x32[t]
+        a = oracle.silu(g) * u
+        errs.append(rel_inf(oracle.bf16_to_f32(hid[r]).astype(np.float64), a))
+    assert max(errs) <= 2e-2, max(errs)
+
+
+# ---------------------------------------------------------------------------
+# FP8 sublayer
+# ---------------------------------------------------------------------------
+def test_fp8_sublayer():
+    w, full, dev, x, bias = gpu_inputs("beam_sublayer_fp8_t8192")
+    print(f"[case] sublayer fp8 T={w.T}", flush=True)
+    cfg = cfg_of(w)
+    h = to_dev_x(w, x)
+    moe_out = torch.empty_like(h)
+    ids = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    bm.beam_moe_sublayer_forward(cfg, h, w.step_k, dev["w_router"], dev["w13"], dev["w2"],
+                                 w13_scale=dev["w13_scale"], w2_scale=dev["w2_scale"], moe_out=moe_out, ids=ids,
+                                 weights=wts)
+    torch.cuda.synchronize()
+    h32 = oracle.bf16_to_f32(x)
+    tok = sample_tokens(w.T)
+    ref = oracle.sublayer_forward(h32, None, None, w.step_k, w.norm_eps, full.w_router, bias, bank_of(w, full),
+                                  w.G, w.Kg, w.K, w.alpha, token_subset=tok)
+    check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    e_moe = rel_inf(moe_out.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
+    e_h = rel_inf(h.float().cpu().numpy()[tok].astype(np.float64), ref["h_new"])
+    print(f"[case] sublayer fp8 moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e}", flush=True)
+    assert e_moe <= TOL[DT_FP8]
+    assert e_h <= TOL[DT_FP8]
+
+
+def test_fp8_forward_decode():
+    """FP8 experts on the decode-sized batch (streaming kernels) against the oracle."""
+    w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192")
+    from dataclasses import replace
+    from beam_inputs import token_inputs, to_bf16_bits
+    w = replace(w0, T=16, sublayer=False, x_recipe="rms_normal")
+    x = to_bf16_bits(token_inputs(w))
+    print("[case] fp8 forward T=16", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, None)
+    x32 = oracle.bf16_to_f32(x)
+    z = oracle.router_logits(x32, full.w_router, None)
+    rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, rid, rw)
+    yref = oracle.moe_combine(x32.astype(np.float64), rid, rw, bank_of(w, full))
+    err = rel_inf(y.float().cpu().numpy().astype(np.float64), yref)
+    print(f"[case] fp8 forward T=16 rel_inf={err:.3e}", flush=True)
+    assert err <= TOL[DT_FP8]
