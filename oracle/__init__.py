@@ -145,12 +145,13 @@ def sigmoidf(z: np.ndarray) -> np.ndarray:
 
 
 def router_logits(x32: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None = None):
-    """z [T,E] FP32: one fused multiply-add chain per (t, e) over h ascending, then + b[e]."""
+    """z [T,E] FP32: 64 contiguous chunks of h, each one ascending fused multiply-add
+    chain; chunk sums added in ascending order; then + b[e]."""
     x32 = np.ascontiguousarray(x32, np.float32)
     wr = np.ascontiguousarray(w_router, np.float32)
     T, H = x32.shape
     H2, E = wr.shape
-    assert H == H2
+    assert H == H2 and H % 64 == 0
     b = None if bias is None else np.ascontiguousarray(bias, np.float32)
     z = np.empty((T, E), np.float32)
     lib().oracle_router_logits(T, H, E, _f32p(x32), _f32p(wr), _f32p(b), _f32p(z))

@@ -17,8 +17,8 @@
  * roundings, as written).  Denormals are not flushed (x86 default).
  *
  * Fixed operation orders (readings where the pages are silent; both are written out
- * in the design notes): the router dot product is one fused multiply-add chain over
- * the hidden index in ascending order; the pre-norm's sum of squares is 64 strided
+ * in the design notes): the router dot product is 64 contiguous fused multiply-add
+ * chains whose sums are added in order; the pre-norm's sum of squares is 64 strided
  * fused chains followed by a fixed pairwise tree.
  */
 #include <math.h>
@@ -87,26 +87,38 @@ void oracle_sigmoidf_array(int64_t n, const float* z, float* s)
 /* ------------------------------------------------------------------------- */
 /*
  * z[t,e] = sum_h x[t,h] * Wr[h,e] (+ bias[e]), FP32.
- * Order contract: acc = 0; for h = 0..H-1: acc = fma(x[t,h], Wr[h,e], acc); then
- * acc + bias[e] as a separate rounded add.  x is FP32 (activations stored in BF16 are
- * widened exactly by the caller).  Wr is [H, E] row-major.
- * The inner loop runs over e so each accumulator still sees h in ascending order.
+ * Order contract (the pages fix FP32 for the router but not the summation order):
+ * the hidden index range is split into 64 contiguous chunks of H/64 entries; chunk c
+ * is one fused multiply-add chain p_c = fma(x[t,h], Wr[h,e], p_c) over its entries in
+ * ascending h, starting from 0; the chunk sums are then added in ascending chunk
+ * order, z = ((p_0 + p_1) + p_2) + ... + p_63, each a single rounded add (0 + p_0 = p_0
+ * exactly); finally z + bias[e], one rounded add.  H must be a multiple of 64.
+ * x is FP32 (activations stored in BF16 are widened exactly by the caller).  Wr is
+ * [H, E] row-major.  The inner loop runs over e so that every accumulator still sees
+ * its own h in ascending order.
  */
 void oracle_router_logits(int64_t T, int H, int E, const float* x, const float* wr,
                           const float* bias, float* z)
 {
+    const int chunk = H / 64;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-        float* acc = z + t * (int64_t)E;
-        for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+        float* acc = (float*)malloc(sizeof(float) * (size_t)E);
+        float* total = z + t * (int64_t)E;
+        for (int e = 0; e < E; ++e) total[e] = 0.0f;
         const float* xr = x + t * (int64_t)H;
-        for (int h = 0; h < H; ++h) {
-            const float xv = xr[h];
-            const float* wrow = wr + (int64_t)h * E;
-            for (int e = 0; e < E; ++e) acc[e] = fmaf(xv, wrow[e], acc[e]);
+        for (int c = 0; c < 64; ++c) {
+            for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+            for (int h = c * chunk; h < (c + 1) * chunk; ++h) {
+                const float xv = xr[h];
+                const float* wrow = wr + (int64_t)h * E;
+                for (int e = 0; e < E; ++e) acc[e] = fmaf(xv, wrow[e], acc[e]);
+            }
+            for (int e = 0; e < E; ++e) total[e] = total[e] + acc[e];
         }
         if (bias)
-            for (int e = 0; e < E; ++e) acc[e] = acc[e] + bias[e];
+            for (int e = 0; e < E; ++e) total[e] = total[e] + bias[e];
+        free(acc);
     }
 }
 

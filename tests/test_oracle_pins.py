@@ -98,22 +98,27 @@ def test_sigmoid_closed_forms():
 # ---------------------------------------------------------------------------
 # router logits
 # ---------------------------------------------------------------------------
-def test_logits_are_one_fused_chain_in_ascending_h_exact_rationals():
-    """Bit-exact against exact rational emulation of acc = fma(x_h, w_h, acc), h
-    ascending, then + bias (one rounding each)."""
+def test_logits_order_contract_exact_rationals():
+    """Bit-exact against exact rational emulation of the order contract: 64 contiguous
+    chunks, each acc = fma(x_h, w_h, acc) over its h ascending, chunk sums added in
+    ascending order, then + bias (one rounding each)."""
     rs = np.random.default_rng(7)
-    T, H, E = 3, 24, 5
+    T, H, E = 2, 192, 3
     x = rs.standard_normal((T, H)).astype(np.float32)
     w = rs.standard_normal((H, E)).astype(np.float32)
     b = rs.standard_normal(E).astype(np.float32)
     z = oracle.router_logits(x, w, b)
+    ch = H // 64
     for t in range(T):
         for e in range(E):
-            acc = 0.0
-            for h in range(H):
-                acc = fma_f32(x[t, h], w[h, e], acc)
-            acc = round_f32(Fraction(acc) + Fraction(float(b[e])))
-            assert z[t, e] == np.float32(acc), (t, e)
+            tot = 0.0
+            for c in range(64):
+                acc = 0.0
+                for h in range(c * ch, (c + 1) * ch):
+                    acc = fma_f32(x[t, h], w[h, e], acc)
+                tot = round_f32(Fraction(tot) + Fraction(acc))
+            tot = round_f32(Fraction(tot) + Fraction(float(b[e])))
+            assert z[t, e] == np.float32(tot), (t, e)
 
 
 def test_logits_within_rounding_bound_of_exact_dot():
