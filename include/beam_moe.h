@@ -23,6 +23,8 @@
  *   - Arguments are validated on the host before anything is enqueued; on error the
  *     call returns a nonzero beam_status and enqueues nothing.  T == 0 returns BEAM_OK
  *     and enqueues nothing.  No C++ exception crosses this boundary.
+ *   - A call that enqueues work first clears the calling thread's last-HIP-error state,
+ *     then returns BEAM_ERR_HIP if any of its own launches failed.
  *   - Calls are reentrant; concurrent calls need distinct workspaces.
  *   - Inputs must be finite; non-finite values are not checked for.
  *   - Results are deterministic: the same inputs give bit-identical outputs.

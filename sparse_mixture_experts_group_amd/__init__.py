@@ -176,6 +176,9 @@ class KernelTimer:
         import torch
         self.kernel, self.n = kernel, n
         self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in self.events:          # torch creates the HIP event on its first record
+            e.record()
+        torch.cuda.synchronize()
         self._arr = (ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in self.events])
 
     def __enter__(self):

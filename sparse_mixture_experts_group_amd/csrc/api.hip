@@ -56,7 +56,7 @@ bool config_supported(const beam_moe_config* c) {
 }
 
 struct Layout {
-    size_t z, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
+    size_t z, zpart, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
     size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm;
     size_t total;
     int nblk, max_tiles;
@@ -74,6 +74,8 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
     L.z = take(sizeof(float) * T * E);
+    // chunk sums of the small-T router kernel (only used below the tiled kernel's range)
+    L.zpart = take(router_uses_partials(T, static_cast<int>(E)) ? sizeof(float) * 64 * T * E : 0);
     L.ids = take(sizeof(int32_t) * P);
     L.wts = take(sizeof(float) * P);
     L.blk_cnt = take(sizeof(int32_t) * L.nblk * E);
@@ -141,6 +143,10 @@ struct Bracket {
     }
 };
 
+// Clears the thread's last-HIP-error state right before the first enqueue, so that the
+// status check after the launches reports only this call's launch failures.
+void clear_hip_error() { (void)hipGetLastError(); }
+
 int launch_status() {
     return hipGetLastError() == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
 }
@@ -153,7 +159,8 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
     float* z = at<float>(ws, L.z);
     {
         Bracket b(BEAM_KERNEL_ROUTER_LOGITS, st);
-        launch_router_logits(st, static_cast<int>(T), c.hidden, E, x_bf16, x_router, w_router, bias, z);
+        launch_router_logits(st, static_cast<int>(T), c.hidden, E, x_bf16, x_router, w_router, bias, z,
+                             at<float>(ws, L.zpart));
     }
     launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, ids, wts,
                          at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
@@ -162,7 +169,7 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
                       at<int32_t>(ws, L.exp_cnt), at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles),
                       at<int32_t>(ws, L.meta), at<int32_t>(ws, L.active));
     launch_route_scatter(st, T * K, K, E, ids, at<int32_t>(ws, L.pair_rank), at<int32_t>(ws, L.blk_off),
-                         at<int32_t>(ws, L.row_of_pair), at<int32_t>(ws, L.pair_of_row));
+                         at<int32_t>(ws, L.exp_off), at<int32_t>(ws, L.row_of_pair), at<int32_t>(ws, L.pair_of_row));
 }
 
 GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, void* ws) {
@@ -269,6 +276,7 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const f
     if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
+    clear_hip_error();
     run_router(*cfg, T, L, ws, st, x, cfg->act_dtype == BEAM_DTYPE_BF16, w_router, logit_bias, ids, weights, false);
     return launch_status();
 }
@@ -295,6 +303,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
     if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
+    clear_hip_error();
     int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
     float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
     const bool bf16_act = cfg->act_dtype == BEAM_DTYPE_BF16;
@@ -329,6 +338,7 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, co
     if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
+    clear_hip_error();
     int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
     float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
     const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3;

@@ -87,4 +87,45 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// Block -> (row tile, column tile) map of the prefill grouped GEMMs.
+// Workgroups are handed to the 8 XCDs round-robin (hardware id i runs on XCD i % 8), and
+// each XCD has its own L2.  Logical block ids are dealt to XCDs in chunks of 32 (one
+// block per CU of an XCD), chunk c going to XCD c % 8, so the blocks one XCD runs at a
+// time are 32 consecutive logical ids.  Logical ids walk groups of kGroupM row tiles
+// across all column tiles, column-major inside a group, so 32 consecutive ids cover
+// 4 row tiles x 8 column tiles: each A tile and each weight panel they read is shared by
+// several blocks of the same XCD.  The grid is a multiple of 256 blocks.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void prefill_tile_of_block(int n_tiles_n, int& tile, int& nt) {
+    const int i = blockIdx.x;
+    const int xcd = i & 7, k = i >> 3;
+    const int L = (((k >> 5) << 3) + xcd) * 32 + (k & 31);
+    const int per_group = kGroupM * n_tiles_n;
+    const int group = L / per_group, rem = L - group * per_group;
+    tile = group * kGroupM + rem % kGroupM;
+    nt = rem / kGroupM;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of the prefill GEMMs: 256 rows x 128 bytes per operand and stage, filled
+// straight from global memory by global_load_lds_dwordx4 (each wave instruction writes
+// 1 KB: lane i lands at destination + 16 i, i.e. 8 rows x 8 chunks of 16 B).  Chunk c
+// of row r is stored in slot c ^ ((r >> 1) & 7), so the 16 rows one fragment read
+// touches per LDS cycle hit distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 256;
+constexpr int kTileRowBytes = 128;
+constexpr int kTileBytes = kTileRows * kTileRowBytes;          // one operand, one stage
+
+__device__ __forceinline__ int tile_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ int tile_offset(int row, int chunk) {
+    return row * kTileRowBytes + (tile_slot(row, chunk) << 4);
+}
+
+// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left alone): the direct-to-LDS loads this wave
+// issued have landed in LDS.
+__device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace beam

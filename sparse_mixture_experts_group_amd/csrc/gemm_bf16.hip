@@ -13,10 +13,10 @@
 //    gate/up) straight from HBM into MFMA B operands with deep unrolling, and the
 //    expert's <= 16 activation rows ride along as the A operand (rows beyond the
 //    expert's count issue no loads).  v_mfma_f32_16x16x32_bf16.
-//  * prefill (many rows per expert): 128 x 128 output tiles from a device-built tile
-//    list, 4 waves each owning 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles, K
-//    staged through LDS 64 at a time with the next K-slab prefetched into registers.
-//    For gate/up the 128 B-rows are 64 gate + 64 up rows of the same columns, so the
+//  * prefill (many rows per expert): 256 x 256 output tiles from a device-built tile
+//    list, 4 waves each owning 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles, K
+//    staged through two LDS stages 64 at a time by direct global->LDS loads.
+//    For gate/up the 256 B-rows are 128 gate + 128 up rows of the same columns, so the
 //    gate and up accumulators of one output land in the same lane and the SwiGLU is
 //    applied in registers.
 #include "common.cuh"
@@ -84,16 +84,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// prefill: LDS-tiled MFMA
+// prefill: LDS-tiled MFMA, 256 x 256 block tile, 128 x 128 per wave
 // ---------------------------------------------------------------------------
+// Each wave owns a 128 x 128 output tile as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles (256
+// FP32 accumulators per lane), so a 16-wide K step reads 8 KB of LDS per wave for 16
+// MFMAs.  K advances 64 at a time through two LDS stages filled by direct global->LDS
+// loads (no register staging): the loads of K tile kt + 1 are issued when tile kt
+// starts and waited for when it ends.
+constexpr int kPfBK = 64;
+constexpr int kPfStageBytes = 2 * kTileBytes;                  // A tile + B tile
+constexpr size_t kPfLdsBytes = 2 * kPfStageBytes;
+
 template <int MODE, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_bf16_prefill(GroupedGemmArgs g) {
-    constexpr int BM = kPrefillBM, BN = 128, BK = 64, LDK = BK + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+    constexpr int BM = kPrefillBM, BN = 256, BK = kPfBK;
+    static_assert(BM == kTileRows && BN == kTileRows && BK * 2 == kTileRowBytes, "tile geometry");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
     const int n_tiles_n = g.n_out / NCOL;
-    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
+    int tile, nt;
+    prefill_tile_of_block(n_tiles_n, tile, nt);
     if (tile >= g.meta[kMetaTiles]) return;
     const int2 ti = g.tiles[tile];
     const int e = ti.x;
@@ -104,83 +114,119 @@ __global__ __launch_bounds__(256) void gemm_bf16_prefill(GroupedGemmArgs g) {
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
 
-    const uint16_t* ap[4];
-    const uint16_t* bp[4];
-    const int kc = (tid & 7) * 8;
+    // Direct-to-LDS assignment: wave w moves rows w*64 + 8 j + lane/8 (j = 0..7) of both
+    // operands; lane i fetches the global chunk that belongs in LDS slot i % 8.
+    const int lr = lane >> 3, ls = lane & 7;
+    const uint8_t* ag[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + i * 32;
+    for (int j = 0; j < 8; ++j) {
+        const int r = wave * 64 + j * 8 + lr;
         const int rr = min(r, rows - 1);
         const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
-        ap[i] = static_cast<const uint16_t*>(g.a) + arow * g.lda + kc;
+        ag[j] = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(g.a) + arow * g.lda) +
+                ((ls ^ ((r >> 1) & 7)) << 4);
+    }
+    // B rows of wave w are affine in j (for gate/up, waves 0-1 move gate rows, 2-3 up rows)
+    const uint8_t* bg;
+    {
+        const int r = wave * 64 + lr;
         int64_t wrow;
-        if (MODE == kGateUp) wrow = (r < BN / 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
+        if (MODE == kGateUp) wrow = (wave < 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
         else wrow = c0 + r;
-        bp[i] = static_cast<const uint16_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * g.kd + kc;
+        bg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * g.kd);
     }
-    u32x4 ra[4], rb[4];
+    const int64_t bstep = 8 * static_cast<int64_t>(g.kd) * 2;      // bytes between j and j + 1
+    // swizzle of row r = w*64 + 8 j + lr: ((r >> 1) & 7) = 4 (j & 1) + (lr >> 1)
+    const int boff_lane[2] = {(ls ^ (lr >> 1)) << 4, (ls ^ (4 + (lr >> 1))) << 4};
+    auto dma = [&](int stage, int k0) {
+        uint8_t* As = smem + stage * kPfStageBytes;
+        uint8_t* Bs = As + kTileBytes;
+        const int kb = k0 * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(ap[i]);
-        rb[i] = *reinterpret_cast<const u32x4*>(bp[i]);
-    }
-    f32x16 acc[2][2];
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_global_load_lds(ag[j] + kb, As + (wave * 64 + j * 8) * kTileRowBytes, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bg + j * bstep + kb + boff_lane[j & 1], Bs + (wave * 64 + j * 8) * kTileRowBytes,
+                                             16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
     const int l32 = lane & 31, lh = lane >> 5;
-    for (int k0 = 0; k0 < g.kd; k0 += BK) {
-        __syncthreads();
+    int arow_l[4], brow_l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid >> 3) + i * 32;
-            *reinterpret_cast<u32x4*>(&As[r * LDK + kc]) = ra[i];
-            *reinterpret_cast<u32x4*>(&Bs[r * LDK + kc]) = rb[i];
-        }
-        __syncthreads();
-        if (k0 + BK < g.kd) {
+    for (int i = 0; i < 4; ++i) {
+        arow_l[i] = wm * 128 + i * 32 + l32;
+        brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
+                                      : wn * 128 + i * 32 + l32;
+    }
+    bf16x8 fa[2][4], fb[2][4];     // fragments, double-buffered over K steps
+    auto load_frags = [&](int buf, int stage, int ks) {
+        const uint8_t* As = smem + stage * kPfStageBytes;
+        const uint8_t* Bs = As + kTileBytes;
+        const int c = ks * 2 + lh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0 + BK);
-                rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0 + BK);
-            }
-        }
+        for (int mi = 0; mi < 4; ++mi)
+            fa[buf][mi] = *reinterpret_cast<const bf16x8*>(As + tile_offset(arow_l[mi], c));
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            fb[buf][ni] = *reinterpret_cast<const bf16x8*>(Bs + tile_offset(brow_l[ni], c));
+    };
+
+    const int nk = g.kd / BK;
+    dma(0, 0);
+    wait_lds_dma();
+    __syncthreads();
+    load_frags(0, 0, 0);
+    // The loop body is branch-free so the scheduling fences apply to whole K steps: the
+    // memory operations of a step are issued first, then its 16 independent MFMAs, and
+    // nothing is hoisted across steps.  The last iteration re-loads the last slab into
+    // the idle stage (clamped index), which nothing reads.
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        dma(stage ^ 1, min(kt + 1, nk - 1) * BK);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[2], bfm[2];
+            const int cur = ks & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < BK / 16) load_frags(cur ^ 1, stage, ks + 1);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + mi * 32 + l32) * LDK + ks * 16 + lh * 8]);
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int brow = (MODE == kGateUp) ? (ni == 0 ? wn * 32 : BN / 2 + wn * 32) : wn * 64 + ni * 32;
-                bfm[ni] = *reinterpret_cast<const bf16x8*>(&Bs[(brow + l32) * LDK + ks * 16 + lh * 8]);
-            }
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfm[ni], acc[mi][ni], 0, 0, 0);
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][mi], fb[cur][ni], acc[mi][ni], 0, 0, 0);
+            if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads first
+            __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);                        // then MFMAs
         }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lds_dma();
+        __syncthreads();
+        load_frags(0, stage ^ 1, 0);
     }
+
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int m = wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            const int m = wm * 128 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
             if (m >= rows) continue;
             uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
             if (MODE == kGateUp) {
-                orow[c0 + wn * 32 + l32] = f32_to_bf16_bits(silu(acc[mi][0][i]) * acc[mi][1][i]);
-            } else {
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    orow[c0 + wn * 64 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i]);
+                    orow[c0 + wn * 64 + ni * 32 + l32] = f32_to_bf16_bits(silu(acc[mi][ni][i]) * acc[mi][ni + 2][i]);
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i]);
             }
         }
     }
@@ -204,16 +250,27 @@ void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArg
 #undef BEAM_DEC
 }
 
+template <int MODE, bool GATHER>
+void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks) {
+    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_prefill<MODE, GATHER>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPfLdsBytes));
+        attr_set = true;
+    }
+    gemm_bf16_prefill<MODE, GATHER><<<blocks, 256, kPfLdsBytes, st>>>(g);
+}
+
 void launch_gemm_bf16_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
     if (g.max_tiles == 0) return;
-    const int ncol = (mode == kGateUp) ? 64 : 128;
-    const int blocks = g.max_tiles * (g.n_out / ncol);
+    const int ncol = (mode == kGateUp) ? 128 : 256;
+    const int blocks = (g.max_tiles * (g.n_out / ncol) + 255) / 256 * 256;   // whole XCD chunks
     if (mode == kGateUp) {
-        if (g.gather) gemm_bf16_prefill<kGateUp, true><<<blocks, 256, 0, st>>>(g);
-        else gemm_bf16_prefill<kGateUp, false><<<blocks, 256, 0, st>>>(g);
+        if (g.gather) launch_prefill_inst<kGateUp, true>(st, g, blocks);
+        else launch_prefill_inst<kGateUp, false>(st, g, blocks);
     } else {
-        if (g.gather) gemm_bf16_prefill<kDown, true><<<blocks, 256, 0, st>>>(g);
-        else gemm_bf16_prefill<kDown, false><<<blocks, 256, 0, st>>>(g);
+        if (g.gather) launch_prefill_inst<kDown, true>(st, g, blocks);
+        else launch_prefill_inst<kDown, false>(st, g, blocks);
     }
 }
 

@@ -7,7 +7,7 @@
 // FP32 accumulator with one fma by the (wave-uniform) weight scale; the row scale is
 // applied once in the epilogue.  Same two shapes and the same SwiGLU fusion as the
 // BF16 kernels (decode: weight streaming with v_mfma_scale_f32_16x16x128_f8f6f4;
-// prefill: 128 x 128 LDS tiles with v_mfma_scale_f32_32x32x64_f8f6f4).
+// prefill: 256 x 256 LDS tiles with v_mfma_scale_f32_32x32x64_f8f6f4).
 #include "common.cuh"
 #include "kernels.h"
 
@@ -113,16 +113,26 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// prefill: 128 x 128 tiles, K blocks of 128 bytes staged through LDS
+// prefill: 256 x 256 block tile, 128 x 128 per wave, K blocks of 128 bytes via LDS
 // ---------------------------------------------------------------------------
+// Same tiling and LDS layout as the BF16 prefill kernel (a 128-entry FP8 K block is the
+// 128-byte row of one LDS tile).  Per K block and per 32 x 32 output tile, two
+// v_mfma_scale_f32_32x32x64_f8f6f4 form the block's partial product in a temporary,
+// which is folded into the accumulator with one fma by the weight-tile scale (uniform
+// over the wave's columns of one weight-scale block).
+constexpr int kF8BK = 128;
+constexpr int kF8StageBytes = 2 * kTileBytes;
+constexpr size_t kF8LdsBytes = 2 * kF8StageBytes;
+
 template <int MODE, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_fp8_prefill(GroupedGemmArgs g) {
-    constexpr int BM = kPrefillBM, BN = 128, BK = 128, LDK = BK + 16;
-    __shared__ __attribute__((aligned(16))) uint8_t As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * LDK];
+    constexpr int BM = kPrefillBM, BN = 256, BK = kF8BK;
+    static_assert(BM == kTileRows && BN == kTileRows && BK == kTileRowBytes, "tile geometry");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;
     const int n_tiles_n = g.n_out / NCOL;
-    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
+    int tile, nt;
+    prefill_tile_of_block(n_tiles_n, tile, nt);
     if (tile >= g.meta[kMetaTiles]) return;
     const int2 ti = g.tiles[tile];
     const int e = ti.x;
@@ -134,116 +144,137 @@ __global__ __launch_bounds__(256) void gemm_fp8_prefill(GroupedGemmArgs g) {
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const int kb_n = g.kd / 128;
 
-    const uint8_t* ap[4];
-    const uint8_t* bp[4];
-    const int kc = (tid & 7) * 16;
+    const int lr = lane >> 3, ls = lane & 7;
+    const uint8_t* ag[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + i * 32;
+    for (int j = 0; j < 8; ++j) {
+        const int r = wave * 64 + j * 8 + lr;
         const int rr = min(r, rows - 1);
         const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
-        ap[i] = static_cast<const uint8_t*>(g.a) + arow * g.lda + kc;
-        int64_t wrow;
-        if (MODE == kGateUp) wrow = (r < BN / 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
-        else wrow = c0 + r;
-        bp[i] = static_cast<const uint8_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * g.kd + kc;
+        ag[j] = static_cast<const uint8_t*>(g.a) + arow * g.lda + ((ls ^ ((r >> 1) & 7)) << 4);
     }
-    // weight-scale rows of this wave's two 32-column groups
-    const float* sw[2];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
+    const uint8_t* bg;
+    {
+        const int r = wave * 64 + lr;
         int64_t wrow;
-        if (MODE == kGateUp) wrow = (ni == 0) ? c0 + wn * 32 : g.n_out + c0 + wn * 32;
-        else wrow = c0 + wn * 64 + ni * 32;
-        sw[ni] = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + wrow / 128) * kb_n;
+        if (MODE == kGateUp) wrow = (wave < 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
+        else wrow = c0 + r;
+        bg = static_cast<const uint8_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * g.kd;
+    }
+    const int64_t bstep = 8 * static_cast<int64_t>(g.kd);
+    const int boff_lane[2] = {(ls ^ (lr >> 1)) << 4, (ls ^ (4 + (lr >> 1))) << 4};
+    auto dma = [&](int stage, int k0) {
+        uint8_t* As = smem8 + stage * kF8StageBytes;
+        uint8_t* Bs = As + kTileBytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_global_load_lds(ag[j] + k0, As + (wave * 64 + j * 8) * kTileRowBytes, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bg + j * bstep + k0 + boff_lane[j & 1],
+                                             Bs + (wave * 64 + j * 8) * kTileRowBytes, 16, 0, 0);
+        }
+    };
+    // weight-scale rows: gate / up blocks (gate-up) or this wave's column block (down)
+    const float* sw0;
+    const float* sw1;
+    if (MODE == kGateUp) {
+        sw0 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_n;
+        sw1 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_n;
+    } else {
+        sw0 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_n;
+        sw1 = sw0;
     }
 
-    u32x4 ra[4], rb[4];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(ap[i]);
-        rb[i] = *reinterpret_cast<const u32x4*>(bp[i]);
-    }
-    f32x16 acc[2][2];
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
     const int l32 = lane & 31, lh = lane >> 5;
-    for (int k0 = 0; k0 < g.kd; k0 += BK) {
-        __syncthreads();
+    int arow_l[4], brow_l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid >> 3) + i * 32;
-            *reinterpret_cast<u32x4*>(&As[r * LDK + kc]) = ra[i];
-            *reinterpret_cast<u32x4*>(&Bs[r * LDK + kc]) = rb[i];
-        }
-        __syncthreads();
-        if (k0 + BK < g.kd) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0 + BK);
-                rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0 + BK);
-            }
-        }
-        const int kb = k0 / 128;
-        const float s0 = sw[0][kb], s1 = sw[1][kb];
-        f32x16 tmp[2][2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) tmp[mi][ni][i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        arow_l[i] = wm * 128 + i * 32 + l32;
+        brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
+                                      : wn * 128 + i * 32 + l32;
+    }
+    // fragment of K half hk: 32 bytes = chunks 4 hk + 2 lh and 4 hk + 2 lh + 1 of the row
+    auto frag = [&](const uint8_t* T, int row, int hk) {
+        const int c = hk * 4 + lh * 2;
+        return join(*reinterpret_cast<const u32x4*>(T + tile_offset(row, c)),
+                    *reinterpret_cast<const u32x4*>(T + tile_offset(row, c + 1)));
+    };
+
+    const int nk = g.kd / BK;
+    dma(0, 0);
+    wait_lds_dma();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        dma(stage ^ 1, min(kt + 1, nk - 1) * BK);
+        const uint8_t* As = smem8 + stage * kF8StageBytes;
+        const uint8_t* Bs = As + kTileBytes;
+        const float s0 = sw0[kt], s1 = sw1[kt];
+        i32x8 af[2][4], bfm[2][4];
 #pragma unroll
         for (int hk = 0; hk < 2; ++hk) {
-            i32x8 af[2], bfm[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
-                const uint8_t* p = &As[(wm * 64 + mi * 32 + l32) * LDK + hk * 64 + lh * 32];
-                af[mi] = join(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
-            }
+            for (int mi = 0; mi < 4; ++mi) af[hk][mi] = frag(As, arow_l[mi], hk);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int brow = (MODE == kGateUp) ? (ni == 0 ? wn * 32 : BN / 2 + wn * 32) : wn * 64 + ni * 32;
-                const uint8_t* p = &Bs[(brow + l32) * LDK + hk * 64 + lh * 32];
-                bfm[ni] = join(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
-            }
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni) tmp[mi][ni] = mfma32_fp8(af[mi], bfm[ni], tmp[mi][ni]);
+            for (int ni = 0; ni < 4; ++ni) bfm[hk][ni] = frag(Bs, brow_l[ni], hk);
         }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                acc[mi][0][i] = fmaf(tmp[mi][0][i], s0, acc[mi][0][i]);
-                acc[mi][1][i] = fmaf(tmp[mi][1][i], s1, acc[mi][1][i]);
+            for (int ni = 0; ni < 4; ++ni) {
+                f32x16 t = {};
+                t = mfma32_fp8(af[0][mi], bfm[0][ni], t);
+                t = mfma32_fp8(af[1][mi], bfm[1][ni], t);
+                const float sc = (MODE == kGateUp) ? (ni < 2 ? s0 : s1) : s0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = fmaf(t[i], sc, acc[mi][ni][i]);
             }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lds_dma();
+        __syncthreads();
     }
+
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int m = wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            const int m = wm * 128 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
             if (m >= rows) continue;
             const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
             const float sa = g.a_scale[ar];
             uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
             if (MODE == kGateUp) {
-                orow[c0 + wn * 32 + l32] = f32_to_bf16_bits(silu(acc[mi][0][i] * sa) * (acc[mi][1][i] * sa));
-            } else {
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    orow[c0 + wn * 64 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
+                    orow[c0 + wn * 64 + ni * 32 + l32] =
+                        f32_to_bf16_bits(silu(acc[mi][ni][i] * sa) * (acc[mi][ni + 2][i] * sa));
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
             }
         }
     }
+}
+
+template <int MODE, bool GATHER>
+void launch_fp8_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks) {
+    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_fp8_prefill<MODE, GATHER>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kF8LdsBytes));
+        attr_set = true;
+    }
+    gemm_fp8_prefill<MODE, GATHER><<<blocks, 256, kF8LdsBytes, st>>>(g);
 }
 
 void launch_gemm_fp8(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool decode) {
@@ -263,14 +294,14 @@ void launch_gemm_fp8(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bo
         return;
     }
     if (g.max_tiles == 0) return;
-    const int ncol = (mode == kGateUp) ? 64 : 128;
-    const int blocks = g.max_tiles * (g.n_out / ncol);
+    const int ncol = (mode == kGateUp) ? 128 : 256;
+    const int blocks = (g.max_tiles * (g.n_out / ncol) + 255) / 256 * 256;   // whole XCD chunks
     if (mode == kGateUp) {
-        if (g.gather) gemm_fp8_prefill<kGateUp, true><<<blocks, 256, 0, st>>>(g);
-        else gemm_fp8_prefill<kGateUp, false><<<blocks, 256, 0, st>>>(g);
+        if (g.gather) launch_fp8_prefill_inst<kGateUp, true>(st, g, blocks);
+        else launch_fp8_prefill_inst<kGateUp, false>(st, g, blocks);
     } else {
-        if (g.gather) gemm_fp8_prefill<kDown, true><<<blocks, 256, 0, st>>>(g);
-        else gemm_fp8_prefill<kDown, false><<<blocks, 256, 0, st>>>(g);
+        if (g.gather) launch_fp8_prefill_inst<kDown, true>(st, g, blocks);
+        else launch_fp8_prefill_inst<kDown, false>(st, g, blocks);
     }
 }
 

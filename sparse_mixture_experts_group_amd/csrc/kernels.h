@@ -5,23 +5,28 @@
 
 namespace beam {
 
-constexpr int kSelectTokens = 32;   // tokens per selection block
+constexpr int kSelectTokens = 16;   // tokens (one per wavefront) per selection block
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 256;
 constexpr int kMetaTiles = 0;       // meta[0]: number of (expert, row-tile) tiles
 constexpr int kMetaActive = 1;      // meta[1]: number of experts with >= 1 row
 constexpr int kMetaInts = 64;
 
-constexpr int kPrefillBM = 128;     // rows per tile of the prefill grouped GEMMs
+constexpr int kPrefillBM = 256;     // rows per tile of the prefill grouped GEMMs
 constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
+
+// The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
+// chunk sums) below this size, the register-tiled kernel above it.
+inline bool router_uses_partials(int64_t T, int E) { return !(E % 128 == 0 && T >= 256); }
 
 inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
 
 enum GemmMode { kGateUp = 0, kDown = 1 };
 
 // router.hip
+// part: [64, T, E] FP32 scratch for the chunk sums of the small-T kernel
 void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
-                          const float* wr, const float* bias, float* z);
+                          const float* wr, const float* bias, float* z, float* part);
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
                           const float* z, int32_t* ids, float* wts, int32_t* blk_cnt,
                           int32_t* pair_rank);
@@ -29,7 +34,7 @@ void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* b
                        int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
                        int32_t* meta, int32_t* active);
 void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const int32_t* ids,
-                          const int32_t* pair_rank, const int32_t* blk_off,
+                          const int32_t* pair_rank, const int32_t* blk_off, const int32_t* exp_off,
                           int32_t* row_of_pair, int32_t* pair_of_row);
 
 // Arguments shared by the grouped GEMM launchers.

@@ -6,11 +6,12 @@
 // picked inside them, weights = scores normalised over the K picks times alpha.  The
 // router runs in FP32 (same page, section "Residual stream ...", last paragraph).
 //
-// Bit-reproducibility: each logit is one fused multiply-add chain over h ascending
-// (no split of the reduction), the sigmoid uses router_exp and IEEE-rounded division,
-// and every ranking is (value desc, index asc), so expert ids are a pure function of
-// the input bits.  Contraction is disabled in this file so that no a*b+c is fused
-// behind our back.
+// Bit-reproducibility: each logit follows one fixed summation order -- the hidden range
+// split into 64 contiguous chunks, each an ascending fused multiply-add chain from 0,
+// the chunk sums added in ascending chunk order, then the bias -- the sigmoid uses
+// router_exp and IEEE-rounded division, and every ranking is (value desc, index asc),
+// so expert ids are a pure function of the input bits.  Contraction is disabled in
+// this file so that no a*b+c is fused behind our back.
 #pragma clang fp contract(off)
 
 #include "common.cuh"
@@ -27,29 +28,75 @@ __device__ __forceinline__ float load_act(const void* x, int64_t i) {
     else return static_cast<const float*>(x)[i];
 }
 
-// One thread per (t, e): for small T, where a tiled kernel would not fill the chip.
+// Small T: one block per (64 experts, 4 chunks, 16 tokens); wave w of the block owns
+// chunk c and lane l expert e, and runs the chunk's fma chain for up to 16 tokens at
+// once.  The block first stages its tokens' slice of x (4 chunks wide) in LDS as FP32,
+// then each lane streams its expert's weights in batches of 16 hidden entries, the next
+// batch in flight while the current one is consumed.  The 64 chunk sums go to `part`
+// [64, T, E] and router_logits_reduce adds them in order.
 template <bool XBF16>
-__global__ __launch_bounds__(64) void router_logits_simple(int T, int H, int E, const void* x,
-                                                           const float* __restrict__ wr,
-                                                           const float* __restrict__ bias,
-                                                           float* __restrict__ z) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= static_cast<int64_t>(T) * E) return;
-    const int t = static_cast<int>(idx / E);
-    const int e = static_cast<int>(idx % E);
-    const int64_t xrow = static_cast<int64_t>(t) * H;
-    float acc = 0.0f;
-#pragma unroll 16
-    for (int h = 0; h < H; ++h)
-        acc = __builtin_fmaf(load_act<XBF16>(x, xrow + h), wr[static_cast<int64_t>(h) * E + e], acc);
-    if (bias) acc = __fadd_rn(acc, bias[e]);
-    z[idx] = acc;
+__global__ __launch_bounds__(256) void router_logits_partial(int T, int H, int E, const void* x,
+                                                             const float* __restrict__ wr,
+                                                             float* __restrict__ part) {
+    extern __shared__ float xs[];             // [16][4 * ch]
+    const int ch = H / 64;
+    const int hw = 4 * ch;
+    const int c0 = blockIdx.y * 4;
+    const int t0 = blockIdx.z * 16;
+    const int nt = min(16, T - t0);
+    for (int i = threadIdx.x; i < 16 * hw; i += 256) {
+        const int tt = i / hw, hh = i - tt * hw;
+        xs[i] = tt < nt ? load_act<XBF16>(x, static_cast<int64_t>(t0 + tt) * H + c0 * ch + hh) : 0.0f;
+    }
+    __syncthreads();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = c0 + w;
+    const int e = blockIdx.x * 64 + (threadIdx.x & 63);
+    if (e >= E) return;
+    const float* xw = xs + w * ch;
+    const float* wcol = wr + static_cast<int64_t>(c) * ch * E + e;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    float wv[16], wn[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) wv[u] = u < ch ? wcol[static_cast<int64_t>(u) * E] : 0.0f;
+    for (int j0 = 0; j0 < ch; j0 += 16) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            wn[u] = (j0 + 16 + u < ch) ? wcol[static_cast<int64_t>(j0 + 16 + u) * E] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (j0 + u < ch) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(xw[i * hw + j0 + u], wv[u], acc[i]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) wv[u] = wn[u];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (i < nt) part[(static_cast<int64_t>(c) * T + t0 + i) * E + e] = acc[i];
 }
 
-// Register-tiled version: block = BT tokens x BE experts, 256 threads as 16 x 16, each
-// thread owns a (BT/16) x (BE/16) accumulator tile and walks h in ascending order, so
-// every accumulator is still a single ascending fma chain.  Tiles of HK hidden
-// entries are staged through LDS (x transposed so a thread's tokens are contiguous).
+__global__ __launch_bounds__(256) void router_logits_reduce(int T, int E, const float* __restrict__ part,
+                                                            const float* __restrict__ bias, float* __restrict__ z) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(T) * E;
+    if (idx >= n) return;
+    float tot = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < 64; ++c) tot = __fadd_rn(tot, part[c * n + idx]);
+    if (bias) tot = __fadd_rn(tot, bias[idx % E]);
+    z[idx] = tot;
+}
+
+// Large T: register-tiled kernel.  Block = BT tokens x BE experts, 256 threads as
+// 16 x 16; each thread owns a (BT/16) x (BE/16) tile of outputs with two registers per
+// output: the running fma chain of the current chunk and the ordered sum of finished
+// chunks.  Tiles of HK hidden entries are staged through LDS (x transposed so a
+// thread's tokens are contiguous).
 template <bool XBF16, int BT, int BE>
 __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, const void* x,
                                                            const float* __restrict__ wr,
@@ -63,15 +110,16 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+    const int ch = H / 64;
 
-    float acc[TM][TN];
+    float acc[TM][TN], tot[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < TN; ++j) { acc[i][j] = 0.0f; tot[i][j] = 0.0f; }
 
     // x tile: BT rows x HK cols = BT*HK/256 elements per thread (contiguous in h)
-    constexpr int XE = BT * HK / 256;         // 8 for BT=64, 4 for BT=32
+    constexpr int XE = BT * HK / 256;
     const int xr = tid / (HK / XE), xc = (tid % (HK / XE)) * XE;
     const int xt = min(t0 + xr, T - 1);
     // w tile: HK rows x BE cols, float4 chunks
@@ -109,6 +157,12 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+            if ((h0 + k + 1) % ch == 0) {          // chunk finished: fold it into the total
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) { tot[i][j] = __fadd_rn(tot[i][j], acc[i][j]); acc[i][j] = 0.0f; }
+            }
         }
     }
 #pragma unroll
@@ -118,7 +172,7 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int e = e0 + tx * TN + j;
-            float v = acc[i][j];
+            float v = tot[i][j];
             if (bias) v = __fadd_rn(v, bias[e]);
             z[static_cast<int64_t>(t) * E + e] = v;
         }
@@ -137,7 +191,7 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
 // permutation, how many of its pairs go to each expert and each pair's rank among the
 // block's pairs with the same expert.
 template <int V>
-__global__ __launch_bounds__(256) void router_select(int T, int E, int G, int Kg, int K,
+__global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E, int G, int Kg, int K,
                                                      float alpha, const float* __restrict__ z,
                                                      int32_t* __restrict__ ids,
                                                      float* __restrict__ wts,
@@ -147,16 +201,17 @@ __global__ __launch_bounds__(256) void router_select(int T, int E, int G, int Kg
     __shared__ int32_t s_cnt[kMaxExperts];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * kSelectTokens;
-    for (int i = threadIdx.x; i < E; i += 256) s_cnt[i] = 0;
+    for (int i = threadIdx.x; i < E; i += kSelectTokens * 64) s_cnt[i] = 0;
 
     const int S = E / G;
     const int L = S / V;
     const int group = (lane * V) / S;
     const bool lane_live = lane * V < E;
 
-    for (int tl = wave; tl < kSelectTokens; tl += 4) {
+    {
+        const int tl = wave;
         const int t = t0 + tl;
-        if (t >= T) break;
+        if (t >= T) goto done;
         float s[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
@@ -221,10 +276,11 @@ __global__ __launch_bounds__(256) void router_select(int T, int E, int G, int Kg
             s_ids[tl * K + lane] = my_id;
         }
     }
+done:
     __syncthreads();
     const int ntok = min(kSelectTokens, T - t0);
     const int np = ntok * K;
-    for (int p = threadIdx.x; p < np; p += 256) {
+    for (int p = threadIdx.x; p < np; p += kSelectTokens * 64) {
         const int e = s_ids[p];
         int r = 0;
         for (int q = 0; q < p; ++q) r += (s_ids[q] == e);
@@ -232,7 +288,7 @@ __global__ __launch_bounds__(256) void router_select(int T, int E, int G, int Kg
         atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < E; i += 256) blk_cnt[static_cast<int64_t>(blockIdx.x) * E + i] = s_cnt[i];
+    for (int i = threadIdx.x; i < E; i += kSelectTokens * 64) blk_cnt[static_cast<int64_t>(blockIdx.x) * E + i] = s_cnt[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -254,32 +310,35 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
     return incl - v;
 }
 
-// One block of 256 threads; thread e owns expert e (E <= 256).
-__global__ __launch_bounds__(256) void route_scan(int nblk, int E, int BM,
-                                                  const int32_t* __restrict__ blk_cnt,
-                                                  int32_t* __restrict__ blk_off,
-                                                  int32_t* __restrict__ exp_cnt,
-                                                  int32_t* __restrict__ exp_off,
-                                                  int2* __restrict__ tiles,
-                                                  int32_t* __restrict__ meta,
-                                                  int32_t* __restrict__ active) {
+// Column scan: block e turns the selection blocks' counts of expert e into exclusive
+// per-block offsets within the expert (blk_off) and the expert's total (exp_cnt).
+__global__ __launch_bounds__(256) void route_col_scan(int nblk, int E, const int32_t* __restrict__ blk_cnt,
+                                                      int32_t* __restrict__ blk_off, int32_t* __restrict__ exp_cnt) {
+    __shared__ int sh[256];
+    const int e = blockIdx.x;
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 256) {
+        const int b = b0 + threadIdx.x;
+        const int v = b < nblk ? blk_cnt[static_cast<int64_t>(b) * E + e] : 0;
+        int tot;
+        const int ex = block_exclusive_scan(v, sh, tot);
+        if (b < nblk) blk_off[static_cast<int64_t>(b) * E + e] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) exp_cnt[e] = carry;
+}
+
+// One block of 256 threads; thread e owns expert e (E <= 256): expert offsets, the
+// (expert, row-tile) list of the grouped GEMMs and the list of experts with rows.
+__global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* __restrict__ exp_cnt,
+                                                  int32_t* __restrict__ exp_off, int2* __restrict__ tiles,
+                                                  int32_t* __restrict__ meta, int32_t* __restrict__ active) {
     __shared__ int sh[256];
     const int e = threadIdx.x;
-    int tot = 0;
-    if (e < E)
-        for (int b = 0; b < nblk; ++b) tot += blk_cnt[static_cast<int64_t>(b) * E + e];
+    const int tot = e < E ? exp_cnt[e] : 0;
     int total_rows;
     const int base = block_exclusive_scan(tot, sh, total_rows);
-    if (e < E) {
-        exp_cnt[e] = tot;
-        exp_off[e] = base;
-        int run = base;
-        for (int b = 0; b < nblk; ++b) {
-            const int64_t i = static_cast<int64_t>(b) * E + e;
-            blk_off[i] = run;
-            run += blk_cnt[i];
-        }
-    }
+    if (e < E) exp_off[e] = base;
     if (e == 0) exp_off[E] = total_rows;
     const int nt = (e < E) ? (tot + BM - 1) / BM : 0;
     int total_tiles;
@@ -299,6 +358,7 @@ __global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int 
                                                      const int32_t* __restrict__ ids,
                                                      const int32_t* __restrict__ pair_rank,
                                                      const int32_t* __restrict__ blk_off,
+                                                     const int32_t* __restrict__ exp_off,
                                                      int32_t* __restrict__ row_of_pair,
                                                      int32_t* __restrict__ pair_of_row) {
     const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -306,7 +366,7 @@ __global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int 
     const int64_t t = p / K;
     const int64_t b = t / kSelectTokens;
     const int e = ids[p];
-    const int row = blk_off[b * E + e] + pair_rank[p];
+    const int row = exp_off[e] + blk_off[b * E + e] + pair_rank[p];
     row_of_pair[p] = row;
     pair_of_row[row] = static_cast<int32_t>(p);
 }
@@ -315,15 +375,14 @@ __global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int 
 // launchers
 // ---------------------------------------------------------------------------
 void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
-                          const float* wr, const float* bias, float* z) {
-    // The tiled kernel needs E % 128 == 0 and H % 32 == 0; it pays off once there
-    // are enough token tiles to fill the chip.
-    const bool tiled = (E % 128 == 0) && (H % 32 == 0) && T >= 256;
-    if (!tiled) {
+                          const float* wr, const float* bias, float* z, float* part) {
+    if (router_uses_partials(T, E)) {
+        dim3 grid((E + 63) / 64, 16, (T + 15) / 16);
+        const size_t lds = sizeof(float) * 16 * 4 * (H / 64);
+        if (x_bf16) router_logits_partial<true><<<grid, 256, lds, st>>>(T, H, E, x, wr, part);
+        else router_logits_partial<false><<<grid, 256, lds, st>>>(T, H, E, x, wr, part);
         const int64_t n = static_cast<int64_t>(T) * E;
-        const int blocks = static_cast<int>((n + 63) / 64);
-        if (x_bf16) router_logits_simple<true><<<blocks, 64, 0, st>>>(T, H, E, x, wr, bias, z);
-        else router_logits_simple<false><<<blocks, 64, 0, st>>>(T, H, E, x, wr, bias, z);
+        router_logits_reduce<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(T, E, part, bias, z);
         return;
     }
     if (T >= 16384) {
@@ -342,22 +401,24 @@ void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, fl
                           int32_t* pair_rank) {
     const int nblk = (T + kSelectTokens - 1) / kSelectTokens;
     const int V = scores_per_lane(E);
-    if (V == 1) router_select<1><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
-    else if (V == 2) router_select<2><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
-    else router_select<4><<<nblk, 256, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+    const int nt = kSelectTokens * 64;
+    if (V == 1) router_select<1><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+    else if (V == 2) router_select<2><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+    else router_select<4><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
 }
 
 void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
                        int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
                        int32_t* meta, int32_t* active) {
-    route_scan<<<1, 256, 0, st>>>(nblk, E, BM, blk_cnt, blk_off, exp_cnt, exp_off, tiles, meta, active);
+    route_col_scan<<<E, 256, 0, st>>>(nblk, E, blk_cnt, blk_off, exp_cnt);
+    route_scan<<<1, 256, 0, st>>>(E, BM, exp_cnt, exp_off, tiles, meta, active);
 }
 
 void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const int32_t* ids,
-                          const int32_t* pair_rank, const int32_t* blk_off,
+                          const int32_t* pair_rank, const int32_t* blk_off, const int32_t* exp_off,
                           int32_t* row_of_pair, int32_t* pair_of_row) {
     const int blocks = static_cast<int>((npairs + 255) / 256);
-    route_scatter<<<blocks, 256, 0, st>>>(npairs, K, E, ids, pair_rank, blk_off, row_of_pair, pair_of_row);
+    route_scatter<<<blocks, 256, 0, st>>>(npairs, K, E, ids, pair_rank, blk_off, exp_off, row_of_pair, pair_of_row);
 }
 
 }  // namespace beam

@@ -109,7 +109,7 @@ def test_tiny_layer_full_parity():
     assert rel_inf(y.cpu().numpy().astype(np.float64), ref["y"]) <= TOL[DT_F32]
 
 
-@pytest.mark.parametrize("T", [1, 5, 33, 100])
+@pytest.mark.parametrize("T", [1, 5, 33, 100, 300])
 def test_tiny_layer_ragged_T(T):
     w, full, dev, x, bias = gpu_inputs("tiny_f32", T)
     print(f"[case] tiny_f32 T={T}", flush=True)
