@@ -42,11 +42,31 @@ def parse():
     p.add_argument("--workload", default="beam_decode_t16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run 3 plain device copies of MIB MiB (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """Plain device-to-device copies of a known size: the profiler's FETCH_SIZE /
+    WRITE_SIZE for these dispatches, divided into the known bytes, give the factor that
+    turns those counters into bytes for the layer's kernels."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this layer is built and timed on a single MI355X; "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -137,7 +157,7 @@ def main():
                 "frac": round(achieved / peak_tf, 4)}
     roof.update({"kernel": "grouped gate/up GEMM + SwiGLU", "kernel_ms": round(gate_up_ms, 4),
                  "algorithmic_bytes": int(gate_up_bytes), "algorithmic_flops": gate_up_flops,
-                 "traffic": None})
+                 "traffic": measured_traffic(w.name)})
 
     # ---- whole-layer figures ----
     layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
@@ -164,6 +184,24 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    passes (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size), or None when there is no record for this workload or the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def cpu_baseline(w, inp, n_tok):

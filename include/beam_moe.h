@@ -70,7 +70,8 @@ typedef enum {
  *   1 <= topk <= min(32, topk_groups * S); routed_scale finite.
  * Kernel support (else BEAM_ERR_UNSUPPORTED):
  *   (act, weight) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
- *   hidden and inter multiples of 64 (of fp8_block for FP8, fp8_block = 128);
+ *   hidden <= 16384; hidden and inter multiples of 64 for F32 weights and of 128
+ *   otherwise (fp8_block must be 128);
  *   with V = ceil(n_experts / 64) scores per lane (V in {1, 2, 4}), S % V == 0 and
  *   S / V a power of two.
  * Beam: {5120, 2560, 256, 8, 4, 8, 2.5f, BF16, BF16 or FP8_E4M3, 128, 1e-6f}.

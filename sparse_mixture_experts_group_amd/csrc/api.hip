@@ -42,6 +42,7 @@ bool config_supported(const beam_moe_config* c) {
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_BF16) ||
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_FP8_E4M3);
     if (!pair_ok) return false;
+    if (c->hidden > 16384) return false;   // LDS staging of the small-batch router kernel
     if (w == BEAM_DTYPE_F32) {
         if (c->hidden % 64 || c->inter % 64) return false;
     } else {
@@ -165,6 +166,14 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
     launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, ids, wts,
                          at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
     if (!permute) return;
+    if (L.nblk <= kFinishSmallBlocks) {
+        launch_route_finish_small(st, static_cast<int>(T), K, E, L.nblk, kPrefillBM, ids, at<int32_t>(ws, L.pair_rank),
+                                  at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off), at<int32_t>(ws, L.exp_cnt),
+                                  at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles), at<int32_t>(ws, L.meta),
+                                  at<int32_t>(ws, L.active), at<int32_t>(ws, L.row_of_pair),
+                                  at<int32_t>(ws, L.pair_of_row));
+        return;
+    }
     launch_route_scan(st, L.nblk, E, kPrefillBM, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off),
                       at<int32_t>(ws, L.exp_cnt), at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles),
                       at<int32_t>(ws, L.meta), at<int32_t>(ws, L.active));

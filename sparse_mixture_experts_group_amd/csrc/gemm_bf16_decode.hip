@@ -1,0 +1,94 @@
+// BF16 grouped expert GEMMs for few rows per expert (decode-sized batches): the GEMM is
+// a weight stream.  MFMA (gfx950) with FP32 accumulation.
+//
+// SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
+// routed per token"; FP32 SwiGLU product per the "Residual stream" section):
+//   gate/up:  h[r, j] = SiLU(a_r . Wg[j]) * (a_r . Wu[j])   (a_r gathered by token)
+//   down:     y[r, n] = h_r . Wd[n]
+// Rows r are the token->expert pairs sorted by expert, so each expert's rows are one
+// contiguous range [exp_off[e], exp_off[e] + exp_cnt[e]).
+//
+// One block per (active expert, 64 output columns); each wave streams 16 weight rows
+// (32 for gate/up) straight from HBM into MFMA B operands with deep unrolling, and the
+// expert's activation rows ride along as the A operand, 16 at a time (rows beyond the
+// expert's count issue no loads).  v_mfma_f32_16x16x32_bf16.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace beam {
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------------------
+// decode: weight streaming
+// ---------------------------------------------------------------------------
+template <int MODE, bool GATHER, int U>
+__global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
+    const int slot = blockIdx.y;
+    if (slot >= g.meta[kMetaActive]) return;
+    const int e = g.active[slot];
+    const int rows = g.exp_cnt[e], row0 = g.exp_off[e];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n0 = (blockIdx.x * 4 + wave) * 16;
+    if (n0 >= g.n_out) return;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
+    const uint16_t* wp = static_cast<const uint16_t*>(g.w) +
+                         (static_cast<int64_t>(e) * nw + n0 + ln) * g.kd + lq * 8;
+    const uint16_t* wu = wp + static_cast<int64_t>(g.n_out) * g.kd;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+
+    for (int m0 = 0; m0 < rows; m0 += 16) {
+        const int m = m0 + ln;
+        const bool mv = m < rows;
+        const int mr = mv ? m : rows - 1;
+        const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
+        const uint16_t* ap = static_cast<const uint16_t*>(g.a) + arow * g.lda + lq * 8;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < g.kd; k += 32 * U) {
+            u32x4 b0[U], b1[U], a[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) b0[u] = *reinterpret_cast<const u32x4*>(wp + k + u * 32);
+            if (MODE == kGateUp) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) b1[u] = *reinterpret_cast<const u32x4*>(wu + k + u * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                a[u] = u32x4{0u, 0u, 0u, 0u};
+                if (mv) a[u] = *reinterpret_cast<const u32x4*>(ap + k + u * 32);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b0[u]), acc0, 0, 0, 0);
+                if (MODE == kGateUp)
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b1[u]), acc1, 0, 0, 0);
+            }
+        }
+        // C[m = lq*4 + i][n = ln]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int mm = m0 + lq * 4 + i;
+            if (mm >= rows) continue;
+            const float v = (MODE == kGateUp) ? silu(acc0[i]) * acc1[i] : acc0[i];
+            out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
+        }
+    }
+}
+
+void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return;
+    dim3 grid((g.n_out + 63) / 64, g.max_active);
+    const bool u8 = (g.kd % 256) == 0;
+#define BEAM_DEC(M, GA, U) gemm_bf16_decode<M, GA, U><<<grid, 256, 0, st>>>(g)
+    if (mode == kGateUp) {
+        if (g.gather) { if (u8) BEAM_DEC(kGateUp, true, 8); else BEAM_DEC(kGateUp, true, 1); }
+        else          { if (u8) BEAM_DEC(kGateUp, false, 8); else BEAM_DEC(kGateUp, false, 1); }
+    } else {
+        if (g.gather) { if (u8) BEAM_DEC(kDown, true, 8); else BEAM_DEC(kDown, true, 1); }
+        else          { if (u8) BEAM_DEC(kDown, false, 8); else BEAM_DEC(kDown, false, 1); }
+    }
+#undef BEAM_DEC
+}
+
+}  // namespace beam

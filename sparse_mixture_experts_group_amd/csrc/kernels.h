@@ -28,11 +28,15 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
                           const float* wr, const float* bias, float* z, float* part);
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
-                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt,
-                          int32_t* pair_rank);
+                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt, int32_t* pair_rank);
 void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
                        int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
                        int32_t* meta, int32_t* active);
+constexpr int kFinishSmallBlocks = 16;   // selection blocks handled by the fused finish kernel
+void launch_route_finish_small(hipStream_t st, int T, int K, int E, int nblk, int BM, const int32_t* ids,
+                               const int32_t* pair_rank, const int32_t* blk_cnt, int32_t* blk_off,
+                               int32_t* exp_cnt, int32_t* exp_off, int2* tiles, int32_t* meta, int32_t* active,
+                               int32_t* row_of_pair, int32_t* pair_of_row);
 void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const int32_t* ids,
                           const int32_t* pair_rank, const int32_t* blk_off, const int32_t* exp_off,
                           int32_t* row_of_pair, int32_t* pair_of_row);
@@ -63,7 +67,7 @@ struct GroupedGemmArgs {
 // gemm_f32.hip (plain FP32, one thread per output)
 void launch_gemm_f32(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int64_t rows,
                      const int32_t* ids);
-// gemm_bf16.hip
+// gemm_bf16_decode.hip / gemm_bf16_prefill.hip
 void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 void launch_gemm_bf16_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 // gemm_fp8.hip

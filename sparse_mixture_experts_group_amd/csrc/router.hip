@@ -44,9 +44,30 @@ __global__ __launch_bounds__(256) void router_logits_partial(int T, int H, int E
     const int c0 = blockIdx.y * 4;
     const int t0 = blockIdx.z * 16;
     const int nt = min(16, T - t0);
-    for (int i = threadIdx.x; i < 16 * hw; i += 256) {
-        const int tt = i / hw, hh = i - tt * hw;
-        xs[i] = tt < nt ? load_act<XBF16>(x, static_cast<int64_t>(t0 + tt) * H + c0 * ch + hh) : 0.0f;
+    // stage x[t0 .. t0+16) x [c0*ch, (c0+4)*ch) as FP32, 4 entries per thread per step
+    // (hw is a multiple of 4); within a batch all loads of a thread are issued before
+    // its LDS stores
+    constexpr int kSteps = 8;
+    for (int base = 0; base < 16 * hw; base += 256 * 4 * kSteps) {
+        float4 v[kSteps];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const int i = base + (threadIdx.x + s * 256) * 4;
+            v[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i < 16 * hw) {
+                const int tt = i / hw, hh = i - tt * hw;
+                if (tt < nt) {
+                    const int64_t src = static_cast<int64_t>(t0 + tt) * H + c0 * ch + hh;
+                    v[s] = make_float4(load_act<XBF16>(x, src), load_act<XBF16>(x, src + 1),
+                                       load_act<XBF16>(x, src + 2), load_act<XBF16>(x, src + 3));
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const int i = base + (threadIdx.x + s * 256) * 4;
+            if (i < 16 * hw) *reinterpret_cast<float4*>(&xs[i]) = v[s];
+        }
     }
     __syncthreads();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -80,14 +101,19 @@ __global__ __launch_bounds__(256) void router_logits_partial(int T, int H, int E
         if (i < nt) part[(static_cast<int64_t>(c) * T + t0 + i) * E + e] = acc[i];
 }
 
+// Ordered sum of the 64 chunk sums (then the bias) for every (t, e); spread over the
+// whole chip, since a few selection waves would need far too long for these loads.
 __global__ __launch_bounds__(256) void router_logits_reduce(int T, int E, const float* __restrict__ part,
                                                             const float* __restrict__ bias, float* __restrict__ z) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t n = static_cast<int64_t>(T) * E;
     if (idx >= n) return;
+    float pv[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) pv[c] = part[c * n + idx];
     float tot = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < 64; ++c) tot = __fadd_rn(tot, part[c * n + idx]);
+#pragma unroll
+    for (int c = 0; c < 64; ++c) tot = __fadd_rn(tot, pv[c]);
     if (bias) tot = __fadd_rn(tot, bias[idx % E]);
     z[idx] = tot;
 }
@@ -353,6 +379,57 @@ __global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* 
     }
 }
 
+// Small batches (at most kFinishSmallBlocks selection blocks): one block does the
+// column scan, the expert scan / tile list / active list and the scatter, in that order,
+// with block barriers in between (saves two launches).
+__global__ __launch_bounds__(256) void route_finish_small(int T, int K, int E, int nblk, int BM,
+                                                          const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ pair_rank,
+                                                          const int32_t* __restrict__ blk_cnt,
+                                                          int32_t* __restrict__ blk_off,
+                                                          int32_t* __restrict__ exp_cnt,
+                                                          int32_t* __restrict__ exp_off, int2* __restrict__ tiles,
+                                                          int32_t* __restrict__ meta, int32_t* __restrict__ active,
+                                                          int32_t* __restrict__ row_of_pair,
+                                                          int32_t* __restrict__ pair_of_row) {
+    __shared__ int sh[256];
+    __shared__ int s_off[kMaxExperts];
+    const int e = threadIdx.x;
+    int tot = 0;
+    if (e < E) {
+        for (int b = 0; b < nblk; ++b) {
+            const int64_t i = static_cast<int64_t>(b) * E + e;
+            blk_off[i] = tot;
+            tot += blk_cnt[i];
+        }
+        exp_cnt[e] = tot;
+    }
+    int total_rows;
+    const int base = block_exclusive_scan(tot, sh, total_rows);
+    if (e < E) { exp_off[e] = base; s_off[e] = base; }
+    if (e == 0) exp_off[E] = total_rows;
+    const int nt = (e < E) ? (tot + BM - 1) / BM : 0;
+    int total_tiles;
+    const int tbase = block_exclusive_scan(nt, sh, total_tiles);
+    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j * BM);
+    int n_active;
+    const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
+    if (e < E && tot > 0) active[abase] = e;
+    if (e == 0) {
+        meta[kMetaTiles] = total_tiles;
+        meta[kMetaActive] = n_active;
+    }
+    __syncthreads();      // blk_off written by this block is read back below
+    const int64_t npairs = static_cast<int64_t>(T) * K;
+    for (int64_t p = threadIdx.x; p < npairs; p += 256) {
+        const int64_t b = (p / K) / kSelectTokens;
+        const int ee = ids[p];
+        const int row = s_off[ee] + blk_off[b * E + ee] + pair_rank[p];
+        row_of_pair[p] = row;
+        pair_of_row[row] = static_cast<int32_t>(p);
+    }
+}
+
 // pair p = t*K + i -> row = offset of (its select block, its expert) + its rank.
 __global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int E,
                                                      const int32_t* __restrict__ ids,
@@ -397,14 +474,15 @@ void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, cons
 }
 
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
-                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt,
-                          int32_t* pair_rank) {
+                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt, int32_t* pair_rank) {
     const int nblk = (T + kSelectTokens - 1) / kSelectTokens;
     const int V = scores_per_lane(E);
     const int nt = kSelectTokens * 64;
-    if (V == 1) router_select<1><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
-    else if (V == 2) router_select<2><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
-    else router_select<4><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank);
+#define BEAM_SEL(VV) router_select<VV><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank)
+    if (V == 1) BEAM_SEL(1);
+    else if (V == 2) BEAM_SEL(2);
+    else BEAM_SEL(4);
+#undef BEAM_SEL
 }
 
 void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
@@ -419,6 +497,14 @@ void launch_route_scatter(hipStream_t st, int64_t npairs, int K, int E, const in
                           int32_t* row_of_pair, int32_t* pair_of_row) {
     const int blocks = static_cast<int>((npairs + 255) / 256);
     route_scatter<<<blocks, 256, 0, st>>>(npairs, K, E, ids, pair_rank, blk_off, exp_off, row_of_pair, pair_of_row);
+}
+
+void launch_route_finish_small(hipStream_t st, int T, int K, int E, int nblk, int BM, const int32_t* ids,
+                               const int32_t* pair_rank, const int32_t* blk_cnt, int32_t* blk_off,
+                               int32_t* exp_cnt, int32_t* exp_off, int2* tiles, int32_t* meta, int32_t* active,
+                               int32_t* row_of_pair, int32_t* pair_of_row) {
+    route_finish_small<<<1, 256, 0, st>>>(T, K, E, nblk, BM, ids, pair_rank, blk_cnt, blk_off, exp_cnt, exp_off,
+                                          tiles, meta, active, row_of_pair, pair_of_row);
 }
 
 }  // namespace beam
