@@ -60,7 +60,7 @@ struct Layout {
     size_t z, zpart, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
     size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm;
     size_t total;
-    int nblk, max_tiles;
+    int nblk, max_tiles, bm;
 };
 
 Layout make_layout(const beam_moe_config& c, int64_t T) {
@@ -71,7 +71,8 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3;
     const bool bf16_act = c.act_dtype == BEAM_DTYPE_BF16;
     L.nblk = static_cast<int>((T + kSelectTokens - 1) / kSelectTokens);
-    L.max_tiles = static_cast<int>((P + kPrefillBM - 1) / kPrefillBM + E);
+    L.bm = prefill_bm(T, static_cast<int>(K), static_cast<int>(E));
+    L.max_tiles = static_cast<int>((P + L.bm - 1) / L.bm + E);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
     L.z = take(sizeof(float) * T * E);
@@ -167,14 +168,14 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
                          at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
     if (!permute) return;
     if (L.nblk <= kFinishSmallBlocks) {
-        launch_route_finish_small(st, static_cast<int>(T), K, E, L.nblk, kPrefillBM, ids, at<int32_t>(ws, L.pair_rank),
+        launch_route_finish_small(st, static_cast<int>(T), K, E, L.nblk, L.bm, ids, at<int32_t>(ws, L.pair_rank),
                                   at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off), at<int32_t>(ws, L.exp_cnt),
                                   at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles), at<int32_t>(ws, L.meta),
                                   at<int32_t>(ws, L.active), at<int32_t>(ws, L.row_of_pair),
                                   at<int32_t>(ws, L.pair_of_row));
         return;
     }
-    launch_route_scan(st, L.nblk, E, kPrefillBM, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off),
+    launch_route_scan(st, L.nblk, E, L.bm, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.blk_off),
                       at<int32_t>(ws, L.exp_cnt), at<int32_t>(ws, L.exp_off), at<int2>(ws, L.tiles),
                       at<int32_t>(ws, L.meta), at<int32_t>(ws, L.active));
     launch_route_scatter(st, T * K, K, E, ids, at<int32_t>(ws, L.pair_rank), at<int32_t>(ws, L.blk_off),
@@ -192,6 +193,7 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     g.meta = at<int32_t>(ws, L.meta);
     g.active = at<int32_t>(ws, L.active);
     g.max_tiles = L.max_tiles;
+    g.bm = L.bm;
     const int64_t P = T * c.topk;
     g.max_active = static_cast<int>(P < c.n_experts ? P : c.n_experts);
     return g;

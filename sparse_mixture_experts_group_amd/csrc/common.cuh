@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -91,20 +92,21 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
 // Workgroups are handed to the 8 XCDs round-robin (hardware id i runs on XCD i % 8), and
 // each XCD has its own L2.  Logical block ids are dealt to XCDs in chunks of 32 (one
 // block per CU of an XCD), chunk c going to XCD c % 8, so the blocks one XCD runs at a
-// time are 32 consecutive logical ids.  Logical ids walk groups of kGroupM row tiles
-// across all column tiles, column-major inside a group, so 32 consecutive ids cover
-// 4 row tiles x 8 column tiles: each A tile and each weight panel they read is shared by
-// several blocks of the same XCD.  The grid is a multiple of 256 blocks.
-constexpr int kGroupM = 4;
-
-__device__ __forceinline__ void prefill_tile_of_block(int n_tiles_n, int& tile, int& nt) {
+// time are 32 consecutive logical ids.  Logical ids walk groups of `group_m` row tiles
+// across all column tiles, column-major inside a group.  group_m = 4 (256-row tiles,
+// MFMA-bound): 32 consecutive ids cover 4 row tiles x 8 column tiles, so A tiles and
+// weight panels are both shared inside an XCD.  group_m = 1 (128-row tiles, bound by
+// streaming weights): consecutive ids are the column tiles of one row tile, so that
+// expert's gathered activation tile stays in the XCD's L2 while its weight panels
+// stream past.  The grid is a multiple of 256 blocks.
+__device__ __forceinline__ void prefill_tile_of_block(int n_tiles_n, int group_m, int& tile, int& nt) {
     const int i = blockIdx.x;
     const int xcd = i & 7, k = i >> 3;
     const int L = (((k >> 5) << 3) + xcd) * 32 + (k & 31);
-    const int per_group = kGroupM * n_tiles_n;
+    const int per_group = group_m * n_tiles_n;
     const int group = L / per_group, rem = L - group * per_group;
-    tile = group * kGroupM + rem % kGroupM;
-    nt = rem / kGroupM;
+    tile = group * group_m + rem % group_m;
+    nt = rem / group_m;
 }
 
 // ---------------------------------------------------------------------------
@@ -124,8 +126,39 @@ __device__ __forceinline__ int tile_offset(int row, int chunk) {
     return row * kTileRowBytes + (tile_slot(row, chunk) << 4);
 }
 
-// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left alone): the direct-to-LDS loads this wave
-// issued have landed in LDS.
-__device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// One wave-wide 16-byte-per-lane direct global->LDS load: lane i's 16 bytes from `src`
+// land at `lds_dst` + 16 i (lds_dst is wave-uniform).  A plain device function, so
+// template code calling it never instantiates the builtin in the host compilation.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt left alone): all but the N most recent
+// direct-to-LDS loads this wave issued have landed in LDS.  gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15 (no wait).
+template <int N>
+__device__ __forceinline__ void wait_lds_dma() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Calls f(std::integral_constant<int, v>{}) for the wave-uniform v in [0, MI] (MI is 2 or
+// 4): a loop body templated on the count of row tiles that hold rows skips the others'
+// work with no branch inside the loop.
+template <int MI, typename F>
+__device__ __forceinline__ void dispatch_row_tiles(int v, F&& f) {
+    static_assert(MI == 2 || MI == 4, "row tiles per wave");
+    if (v >= MI) {
+        f(std::integral_constant<int, MI>{});
+    } else if (v <= 0) {
+        f(std::integral_constant<int, 0>{});
+    } else if constexpr (MI == 4) {
+        if (v == 1) f(std::integral_constant<int, 1>{});
+        else if (v == 2) f(std::integral_constant<int, 2>{});
+        else f(std::integral_constant<int, 3>{});
+    } else {
+        f(std::integral_constant<int, 1>{});
+    }
+}
 
 }  // namespace beam

@@ -12,7 +12,11 @@ constexpr int kMetaTiles = 0;       // meta[0]: number of (expert, row-tile) til
 constexpr int kMetaActive = 1;      // meta[1]: number of experts with >= 1 row
 constexpr int kMetaInts = 64;
 
-constexpr int kPrefillBM = 256;     // rows per tile of the prefill grouped GEMMs
+// Rows per tile of the prefill grouped GEMMs: 256, or 128 when the average expert has
+// fewer than ~192 rows (less padding where the GEMM is bound by streaming weights).
+constexpr int kPrefillBMMax = 256;
+constexpr int kPrefillBMMin = 128;
+inline int prefill_bm(int64_t T, int K, int E) { return T * K < 192LL * E ? kPrefillBMMin : kPrefillBMMax; }
 constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
@@ -59,6 +63,7 @@ struct GroupedGemmArgs {
     const int32_t* meta;      // meta[kMetaTiles], meta[kMetaActive]
     const int32_t* active;    // [E] experts with rows, ascending
     int max_tiles;            // grid bound for tile-driven kernels
+    int bm;                   // rows per tile of the tile list (prefill kernels)
     int max_active;           // grid bound for expert-driven kernels
     void* out;                // [rows, n_out]
     int64_t ldo;              // elements per output row
