@@ -142,6 +142,16 @@ __device__ __forceinline__ void wait_lds_dma() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier for the direct-to-LDS pipelines.  __syncthreads() carries a
+// workgroup release fence, which waits for every outstanding vector-memory operation
+// (vmcnt(0)) and so would drain the loads of all stages in flight.  Here each wave
+// first waits for its own loads of the stage about to be read (wait_lds_dma), then for
+// its own LDS reads (so no wave overwrites a stage another wave still reads), then
+// meets the others.  The asm statement is also a compiler memory barrier.
+__device__ __forceinline__ void lds_pipeline_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Calls f(std::integral_constant<int, v>{}) for the wave-uniform v in [0, MI] (MI is 2 or
 // 4): a loop body templated on the count of row tiles that hold rows skips the others'
 // work with no branch inside the loop.

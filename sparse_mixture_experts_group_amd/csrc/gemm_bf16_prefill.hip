@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_prefill(GroupedGemmArgs g) {
 #pragma unroll
         for (int s0 = 0; s0 < NST - 1; ++s0) dma(s0, min(s0, nk - 1) * BK);
         wait_lds_dma<(NST - 2) * PER>();
-        __syncthreads();
+        lds_pipeline_barrier();
         load_frags(0, 0, 0);
         // The loop body is branch-free so the scheduling fences apply to whole K steps: the
         // memory operations of a step are issued first, then its independent MFMAs, and
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_prefill(GroupedGemmArgs g) {
             }
             __builtin_amdgcn_sched_barrier(0);
             wait_lds_dma<(NST - 2) * PER>();
-            __syncthreads();
+            lds_pipeline_barrier();
             load_frags(0, nstage, 0);
             stage = nstage;
         }

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_prefill(GroupedGemmArgs g) {
     const int nk = g.kd / BK;
     dma(0, 0);
     wait_lds_dma<0>();
-    __syncthreads();
+    lds_pipeline_barrier();
     // two-stage pipeline, branch-free body: the last iteration re-loads the last block
     // into the idle stage (clamped index), which nothing reads
     // The K loop is instantiated per count of live row tiles, so no instance tests them.
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_prefill(GroupedGemmArgs g) {
             dma(stage ^ 1, min(kt + 1, nk - 1) * BK);
             k_block(mv_tag, stage, sw0[kt], sw1[kt]);
             wait_lds_dma<0>();
-            __syncthreads();
+            lds_pipeline_barrier();
         }
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
