@@ -103,15 +103,19 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
 def quantize_e4m3_blocks(w: np.ndarray, block: int = 128):
     """Block-scaled E4M3 quantisation of a [N, K] float32 matrix.
 
-    Each block x block tile gets one float32 scale = amax / 448 (1 for an all-zero
-    tile); codes = E4M3(w / scale).  Returns (codes uint8 [N, K], scales float32
-    [N/block, K/block]).
+    Each block x block tile gets one power-of-two float32 scale, the smallest with
+    amax / scale <= 448 (1 for an all-zero tile), so the scale is exactly an E8M0
+    block exponent; codes = E4M3(w / scale), with amax / scale in (224, 448].
+    Returns (codes uint8 [N, K], scales float32 [N/block, K/block]).
     """
     n, k = w.shape
     assert n % block == 0 and k % block == 0
     t = w.reshape(n // block, block, k // block, block)
-    amax = np.abs(t).max(axis=(1, 3)).astype(np.float32)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    amax = np.abs(t).max(axis=(1, 3)).astype(np.float64)
+    # ceil(log2(amax / 448)) from the exact binary exponent: frexp gives m in [0.5, 1)
+    m, ex = np.frexp(amax / E4M3_MAX)
+    ex = np.where(m == 0.5, ex - 1, ex)
+    scale = np.where(amax > 0, np.ldexp(1.0, ex), 1.0).astype(np.float32)
     scaled = (t / scale[:, None, :, None]).astype(np.float32)
     codes = encode_e4m3(scaled).reshape(n, k)
     return codes, scale

@@ -60,7 +60,7 @@ typedef enum {
 typedef enum {
     BEAM_DTYPE_F32 = 0,
     BEAM_DTYPE_BF16 = 1,
-    BEAM_DTYPE_FP8_E4M3 = 2     /* OCP E4M3FN, block-scaled with FP32 scales */
+    BEAM_DTYPE_FP8_E4M3 = 2     /* OCP E4M3FN, block-scaled (power-of-two FP32 scales) */
 } beam_dtype;
 
 /*
@@ -124,9 +124,11 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  *   w13        device [E, 2I, H] weight_dtype: rows 0..I-1 gate, rows I..2I-1 up,
  *              each row H-contiguous
  *   w13_scale  FP8 only: device [E, 2I/128, H/128] FP32 block scales (value =
- *              code * scale of its 128x128 tile); must be NULL otherwise
+ *              code * scale of its 128x128 tile); must be NULL otherwise.  Each
+ *              scale must be a normal power of two (an E8M0 block exponent): above
+ *              32 tokens the matrix cores apply only its exponent field.
  *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous)
- *   w2_scale   FP8 only: device [E, H/128, I/128] FP32; NULL otherwise
+ *   w2_scale   FP8 only: device [E, H/128, I/128] FP32 powers of two; NULL otherwise
  *   y          device [T, H] act_dtype out
  *   ids_out    device [T, K] int32 out, or NULL;  weights_out device [T, K] FP32 or NULL
  * With FP8 weights the activations entering each GEMM are quantised on the GPU to E4M3

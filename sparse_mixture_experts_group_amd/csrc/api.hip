@@ -71,7 +71,7 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3;
     const bool bf16_act = c.act_dtype == BEAM_DTYPE_BF16;
     L.nblk = static_cast<int>((T + kSelectTokens - 1) / kSelectTokens);
-    L.bm = prefill_bm(T, static_cast<int>(K), static_cast<int>(E));
+    L.bm = kPrefillBM;
     L.max_tiles = static_cast<int>((P + L.bm - 1) / L.bm + E);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
@@ -223,19 +223,27 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) launch_gemm_bf16_decode(st, kGateUp, g1);
-            else launch_gemm_bf16_prefill(st, kGateUp, g1);
+            else launch_gemm_prefill(st, kGateUp, g1, false);
         }
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) launch_gemm_bf16_decode(st, kDown, g2);
-            else launch_gemm_bf16_prefill(st, kDown, g2);
+            else launch_gemm_prefill(st, kDown, g2, false);
         }
     } else {
-        { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_fp8(st, kGateUp, g1, decode); }
+        {
+            Bracket b(BEAM_KERNEL_GATE_UP, st);
+            if (decode) launch_gemm_fp8_decode(st, kGateUp, g1);
+            else launch_gemm_prefill(st, kGateUp, g1, true);
+        }
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
-        { Bracket b(BEAM_KERNEL_DOWN, st); launch_gemm_fp8(st, kDown, g2, decode); }
+        {
+            Bracket b(BEAM_KERNEL_DOWN, st);
+            if (decode) launch_gemm_fp8_decode(st, kDown, g2);
+            else launch_gemm_prefill(st, kDown, g2, true);
+        }
     }
 }
 

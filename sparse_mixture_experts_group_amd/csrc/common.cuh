@@ -110,20 +110,22 @@ __device__ __forceinline__ void prefill_tile_of_block(int n_tiles_n, int group_m
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles of the prefill GEMMs: 256 rows x 128 bytes per operand and stage, filled
-// straight from global memory by global_load_lds_dwordx4 (each wave instruction writes
-// 1 KB: lane i lands at destination + 16 i, i.e. 8 rows x 8 chunks of 16 B).  Chunk c
-// of row r is stored in slot c ^ ((r >> 1) & 7), so the 16 rows one fragment read
-// touches per LDS cycle hit distinct banks.
+// LDS stages of the prefill GEMMs: each operand row holds 64 bytes of K (32 BF16 or 64
+// FP8 values) per stage, filled straight from global memory by global_load_lds_dwordx4.
+// One wave instruction writes 1 KB: lane i lands at destination + 16 i, i.e. 16 rows x
+// 4 chunks of 16 B.  Chunk c of row r is stored in slot c ^ ((r >> 2) & 3): the 16 rows
+// one fragment read serves per LDS cycle (same chunk) then cover all 64 banks.
 // ---------------------------------------------------------------------------
-constexpr int kTileRows = 256;
-constexpr int kTileRowBytes = 128;
-constexpr int kTileBytes = kTileRows * kTileRowBytes;          // one operand, one stage
+constexpr int kStageRowBytes = 64;
 
-__device__ __forceinline__ int tile_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int stage_offset(int row, int chunk) {
+    return row * kStageRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
 
-__device__ __forceinline__ int tile_offset(int row, int chunk) {
-    return row * kTileRowBytes + (tile_slot(row, chunk) << 4);
+// Global byte offset, inside a row's 64-byte K slab, of the chunk lane `lane` moves: a
+// DMA instruction covers rows base + lane / 4 (base a multiple of 16), slot lane % 4.
+__device__ __forceinline__ int dma_chunk_offset(int lane) {
+    return ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
 }
 
 // One wave-wide 16-byte-per-lane direct global->LDS load: lane i's 16 bytes from `src`
@@ -150,6 +152,27 @@ __device__ __forceinline__ void wait_lds_dma() {
 // meets the others.  The asm statement is also a compiler memory barrier.
 __device__ __forceinline__ void lds_pipeline_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The same wait again as a builtin (a no-op here) so the compiler's wait tracking
+    // knows every earlier LDS read has completed and adds no waits for them later.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Scheduling pattern for one K step of an MFMA loop: NM MFMAs, the first NR of them each
+// followed by one LDS read and the next NV each by one global (direct-to-LDS) load, so
+// the reads and loads issue while the matrix pipe is busy.  Leftover reads and loads
+// follow the last MFMA.
+template <int NM, int NR, int NV>
+__device__ __forceinline__ void sched_interleave() {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
+        else if (i < NR + NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+#pragma unroll
+    for (int i = NM; i < NR; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = (NM > NR ? NM : NR); i < NR + NV; ++i) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
 }
 
 // Calls f(std::integral_constant<int, v>{}) for the wave-uniform v in [0, MI] (MI is 2 or

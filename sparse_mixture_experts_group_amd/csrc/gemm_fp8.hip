@@ -1,13 +1,13 @@
-// FP8 (OCP E4M3FN) grouped expert GEMMs on the gfx950 f8f6f4 MFMA, FP32 accumulation.
+// FP8 (OCP E4M3FN) grouped expert GEMMs for few rows per expert (decode) on the gfx950
+// f8f6f4 MFMA, FP32 accumulation.
 //
 // Weights carry one FP32 scale per 128 x 128 tile (value = code * scale); activations
 // are quantised on the GPU with one FP32 scale per row (amax / 448).  The reduction is
 // split into 128-wide K blocks, one weight-scale block each: the block's partial
 // product is formed on the matrix core with unit hardware scales and folded into the
 // FP32 accumulator with one fma by the (wave-uniform) weight scale; the row scale is
-// applied once in the epilogue.  Same two shapes and the same SwiGLU fusion as the
-// BF16 kernels (decode: weight streaming with v_mfma_scale_f32_16x16x128_f8f6f4;
-// prefill: BM x 256 LDS tiles with v_mfma_scale_f32_32x32x64_f8f6f4).
+// applied once in the epilogue.  Weight streaming with v_mfma_scale_f32_16x16x128_f8f6f4
+// and the same SwiGLU fusion as the BF16 decode kernel.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -28,9 +28,6 @@ __device__ __forceinline__ f32x4 mfma16_fp8(i32x8 a, i32x8 b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, kUnitScale, 0, kUnitScale);
 }
 
-__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -112,256 +109,19 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// prefill: 256 x 256 block tile, 128 x 128 per wave, K blocks of 128 bytes via LDS
-// ---------------------------------------------------------------------------
-// Same tiling and LDS layout as the BF16 prefill kernel (a 128-entry FP8 K block is the
-// 128-byte row of one LDS tile).  Per K block and per 32 x 32 output tile, two
-// v_mfma_scale_f32_32x32x64_f8f6f4 form the block's partial product in a temporary,
-// which is folded into the accumulator with one fma by the weight-tile scale (uniform
-// over the wave's columns of one weight-scale block).
-constexpr int kF8BK = 128;
-template <int BM> constexpr int f8_stage_bytes() { return (BM + kTileRows) * kTileRowBytes; }
-template <int BM> constexpr size_t f8_lds_bytes() { return 2 * f8_stage_bytes<BM>(); }
-
-// BM = 256: each wave owns 128 rows (4 MFMA row tiles); BM = 128: 64 rows (2 row tiles).
-template <int MODE, bool GATHER, int BM>
-__global__ __launch_bounds__(256) void gemm_fp8_prefill(GroupedGemmArgs g) {
-    constexpr int BN = 256, BK = kF8BK, MI = BM / 64, WROWS = BM / 2;
-    constexpr int kF8StageBytes = f8_stage_bytes<BM>();
-    static_assert((BM == 256 || BM == 128) && BN == kTileRows && BK == kTileRowBytes, "tile geometry");
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
-    constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;
-    const int n_tiles_n = g.n_out / NCOL;
-    int tile, nt;
-    prefill_tile_of_block(n_tiles_n, BM == 256 ? 4 : 1, tile, nt);
-    if (tile >= g.meta[kMetaTiles]) return;
-    const int2 ti = g.tiles[tile];
-    const int e = ti.x;
-    const int rows = min(BM, g.exp_cnt[e] - ti.y);
-    const int row0 = g.exp_off[e] + ti.y;
-    const int c0 = nt * NCOL;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
-    const int kb_n = g.kd / 128;
-
-    const int lr = lane >> 3, ls = lane & 7;
-    constexpr int AJ = BM / 32;
-    const uint8_t* ag[AJ];
-#pragma unroll
-    for (int j = 0; j < AJ; ++j) {
-        const int r = wave * (BM / 4) + j * 8 + lr;
-        const int rr = min(r, rows - 1);
-        const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
-        ag[j] = static_cast<const uint8_t*>(g.a) + arow * g.lda + ((ls ^ ((r >> 1) & 7)) << 4);
-    }
-    const uint8_t* bg;
-    {
-        const int r = wave * 64 + lr;
-        int64_t wrow;
-        if (MODE == kGateUp) wrow = (wave < 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
-        else wrow = c0 + r;
-        bg = static_cast<const uint8_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * g.kd;
-    }
-    const int64_t bstep = 8 * static_cast<int64_t>(g.kd);
-    const int boff_lane[2] = {(ls ^ (lr >> 1)) << 4, (ls ^ (4 + (lr >> 1))) << 4};
-    auto dma = [&](int stage, int k0) {
-        uint8_t* As = smem8 + stage * kF8StageBytes;
-        uint8_t* Bs = As + BM * kTileRowBytes;
-#pragma unroll
-        for (int j = 0; j < AJ; ++j)
-            lds_dma16(ag[j] + k0, As + (wave * (BM / 4) + j * 8) * kTileRowBytes);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            lds_dma16(bg + j * bstep + k0 + boff_lane[j & 1], Bs + (wave * 64 + j * 8) * kTileRowBytes);
-    };
-    // weight-scale rows: gate / up blocks (gate-up) or this wave's column block (down)
-    const float* sw0;
-    const float* sw1;
-    if (MODE == kGateUp) {
-        sw0 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_n;
-        sw1 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_n;
-    } else {
-        sw0 = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_n;
-        sw1 = sw0;
-    }
-
-    f32x16 acc[MI][4];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-
-    const int l32 = lane & 31, lh = lane >> 5;
-    int arow_l[MI], brow_l[4];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) arow_l[i] = wm * WROWS + i * 32 + l32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
-                                      : wn * 128 + i * 32 + l32;
-    }
-    // 32-row MFMA tiles of this wave that hold rows of the expert (wave-uniform): the
-    // others (padding of an expert's last tile) skip their LDS reads, MFMAs and folds.
-    const int mvalid = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * WROWS + 31) / 32)));
-    // fragment of K half hk: 32 bytes = chunks 4 hk + 2 lh and 4 hk + 2 lh + 1 of the row
-    auto frag = [&](const uint8_t* T, int row, int hk) {
-        const int c = hk * 4 + lh * 2;
-        return join(*reinterpret_cast<const u32x4*>(T + tile_offset(row, c)),
-                    *reinterpret_cast<const u32x4*>(T + tile_offset(row, c + 1)));
-    };
-
-    // One K block (128 bytes) from LDS stage `stage`, as 2*MI groups of (one row tile,
-    // two column tiles).  The 4 MFMAs of group q go to temporary set q & 1 while the 32
-    // FMAs folding group q - 1 (scale of its weight block) run: MFMA and VALU overlap,
-    // and each fold reads results issued a whole group earlier.
-    auto k_block = [&](auto mv_tag, int stage, float s0, float s1) {
-        constexpr int MV = decltype(mv_tag)::value;
-        const uint8_t* As = smem8 + stage * kF8StageBytes;
-        const uint8_t* Bs = As + BM * kTileRowBytes;
-        i32x8 bfm[2][4];
-#pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bfm[hk][ni] = frag(Bs, brow_l[ni], hk);
-        i32x8 af[2][2];
-        f32x16 t[2][2];
-        constexpr int NG = 2 * MI;
-#pragma unroll
-        for (int q = 0; q <= NG; ++q) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (q < NG && (q >> 1) < MV) {
-                const int mi = q >> 1, np = q & 1;
-                if (np == 0) {
-#pragma unroll
-                    for (int hk = 0; hk < 2; ++hk) af[mi & 1][hk] = frag(As, arow_l[mi], hk);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x16 z = {};
-                    t[q & 1][j] = mfma32_fp8(af[mi & 1][0], bfm[0][2 * np + j], z);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    t[q & 1][j] = mfma32_fp8(af[mi & 1][1], bfm[1][2 * np + j], t[q & 1][j]);
-            }
-            if (q > 0 && ((q - 1) >> 1) < MV) {
-                const int p = q - 1, mi = p >> 1, np = p & 1;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int ni = 2 * np + j;
-                    const float sc = (MODE == kGateUp) ? (ni < 2 ? s0 : s1) : s0;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[mi][ni][i] = fmaf(t[p & 1][j][i], sc, acc[mi][ni][i]);
-                }
-            }
-            if (q < NG && q > 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    constexpr int PER = AJ + 8;       // direct-to-LDS loads per K block per wave
-    const int nk = g.kd / BK;
-    dma(0, 0);
-    wait_lds_dma<0>();
-    lds_pipeline_barrier();
-    // two-stage pipeline, branch-free body: the last iteration re-loads the last block
-    // into the idle stage (clamped index), which nothing reads
-    // The K loop is instantiated per count of live row tiles, so no instance tests them.
-    auto k_loop = [&](auto mv_tag) {
-        for (int kt = 0; kt < nk; ++kt) {
-            const int stage = kt & 1;
-            __builtin_amdgcn_sched_barrier(0);
-            dma(stage ^ 1, min(kt + 1, nk - 1) * BK);
-            k_block(mv_tag, stage, sw0[kt], sw1[kt]);
-            wait_lds_dma<0>();
-            lds_pipeline_barrier();
-        }
-    };
-    dispatch_row_tiles<MI>(mvalid, k_loop);
-    (void)PER;
-
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = wm * WROWS + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
-            if (m >= rows) continue;
-            const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
-            const float sa = g.a_scale[ar];
-            uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
-            if (MODE == kGateUp) {
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    orow[c0 + wn * 64 + ni * 32 + l32] =
-                        f32_to_bf16_bits(silu(acc[mi][ni][i] * sa) * (acc[mi][ni + 2][i] * sa));
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
-            }
-        }
-    }
-}
-
-template <int MODE, bool GATHER, int BM>
-void launch_fp8_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks) {
-    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_fp8_prefill<MODE, GATHER, BM>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(f8_lds_bytes<BM>()));
-        attr_set = true;
-    }
-    gemm_fp8_prefill<MODE, GATHER, BM><<<blocks, 256, f8_lds_bytes<BM>(), st>>>(g);
-}
-
-void launch_gemm_fp8(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool decode) {
-    if (decode) {
-        if (g.max_active == 0) return;
-        dim3 grid((g.n_out + 63) / 64, g.max_active);
-        const bool u4 = (g.kd % 512) == 0;
+void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return;
+    dim3 grid((g.n_out + 63) / 64, g.max_active);
+    const bool u4 = (g.kd % 512) == 0;
 #define BEAM_DEC(M, GA, U) gemm_fp8_decode<M, GA, U><<<grid, 256, 0, st>>>(g)
-        if (mode == kGateUp) {
-            if (g.gather) { if (u4) BEAM_DEC(kGateUp, true, 4); else BEAM_DEC(kGateUp, true, 1); }
-            else          { if (u4) BEAM_DEC(kGateUp, false, 4); else BEAM_DEC(kGateUp, false, 1); }
-        } else {
-            if (g.gather) { if (u4) BEAM_DEC(kDown, true, 4); else BEAM_DEC(kDown, true, 1); }
-            else          { if (u4) BEAM_DEC(kDown, false, 4); else BEAM_DEC(kDown, false, 1); }
-        }
-#undef BEAM_DEC
-        return;
-    }
-    if (g.max_tiles == 0) return;
-    const int ncol = (mode == kGateUp) ? 128 : 256;
-    const int blocks = (g.max_tiles * (g.n_out / ncol) + 255) / 256 * 256;   // whole XCD chunks
-    const bool small = g.bm == kPrefillBMMin;
     if (mode == kGateUp) {
-        if (g.gather) {
-            if (small) launch_fp8_prefill_inst<kGateUp, true, kPrefillBMMin>(st, g, blocks);
-            else launch_fp8_prefill_inst<kGateUp, true, kPrefillBMMax>(st, g, blocks);
-        } else {
-            if (small) launch_fp8_prefill_inst<kGateUp, false, kPrefillBMMin>(st, g, blocks);
-            else launch_fp8_prefill_inst<kGateUp, false, kPrefillBMMax>(st, g, blocks);
-        }
+        if (g.gather) { if (u4) BEAM_DEC(kGateUp, true, 4); else BEAM_DEC(kGateUp, true, 1); }
+        else          { if (u4) BEAM_DEC(kGateUp, false, 4); else BEAM_DEC(kGateUp, false, 1); }
     } else {
-        if (g.gather) {
-            if (small) launch_fp8_prefill_inst<kDown, true, kPrefillBMMin>(st, g, blocks);
-            else launch_fp8_prefill_inst<kDown, true, kPrefillBMMax>(st, g, blocks);
-        } else {
-            if (small) launch_fp8_prefill_inst<kDown, false, kPrefillBMMin>(st, g, blocks);
-            else launch_fp8_prefill_inst<kDown, false, kPrefillBMMax>(st, g, blocks);
-        }
+        if (g.gather) { if (u4) BEAM_DEC(kDown, true, 4); else BEAM_DEC(kDown, true, 1); }
+        else          { if (u4) BEAM_DEC(kDown, false, 4); else BEAM_DEC(kDown, false, 1); }
     }
+#undef BEAM_DEC
 }
 
 }  // namespace beam

@@ -14,9 +14,18 @@ constexpr int kMetaInts = 64;
 
 // Rows per tile of the prefill grouped GEMMs: 256, or 128 when the average expert has
 // fewer than ~192 rows (less padding where the GEMM is bound by streaming weights).
-constexpr int kPrefillBMMax = 256;
-constexpr int kPrefillBMMin = 128;
-inline int prefill_bm(int64_t T, int K, int E) { return T * K < 192LL * E ? kPrefillBMMin : kPrefillBMMax; }
+constexpr int kPrefillBM = 256;     // rows per tile of the prefill grouped GEMMs
+// Tiles of an expert with n routed rows for the prefill GEMMs: ceil(n / BM) tiles of
+// whole 32-row blocks, as equal as possible (so the tiles of one expert carry the same
+// work and stream its weights in step).  Tile j holds rows [first(j), first(j + 1)),
+// first(count) = n.  The tile list stores (expert, j).
+__host__ __device__ inline int expert_tile_count(int n, int BM) { return (n + BM - 1) / BM; }
+__host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
+    const int nt = expert_tile_count(n, BM);
+    if (j >= nt) return n;
+    const int64_t m = (n + 31) / 32;
+    return static_cast<int>((j * m / nt) * 32);
+}
 constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
@@ -59,7 +68,7 @@ struct GroupedGemmArgs {
     int kd;                   // reduction length
     const int32_t* exp_cnt;   // [E]
     const int32_t* exp_off;   // [E+1]
-    const int2* tiles;        // [max_tiles] (expert, first row within expert)
+    const int2* tiles;        // [max_tiles] (expert, tile of the expert)
     const int32_t* meta;      // meta[kMetaTiles], meta[kMetaActive]
     const int32_t* active;    // [E] experts with rows, ascending
     int max_tiles;            // grid bound for tile-driven kernels
@@ -72,11 +81,11 @@ struct GroupedGemmArgs {
 // gemm_f32.hip (plain FP32, one thread per output)
 void launch_gemm_f32(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int64_t rows,
                      const int32_t* ids);
-// gemm_bf16_decode.hip / gemm_bf16_prefill.hip
+// gemm_bf16_decode.hip / gemm_fp8.hip: few rows per expert, weight streaming
 void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
-void launch_gemm_bf16_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
-// gemm_fp8.hip
-void launch_gemm_fp8(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool decode);
+void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// gemm_prefill.hip: 256 x 256 LDS-tiled MFMA, BF16 or FP8 operands
+void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8);
 
 // elementwise.hip
 void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,

@@ -366,10 +366,10 @@ __global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* 
     const int base = block_exclusive_scan(tot, sh, total_rows);
     if (e < E) exp_off[e] = base;
     if (e == 0) exp_off[E] = total_rows;
-    const int nt = (e < E) ? (tot + BM - 1) / BM : 0;
+    const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
     int total_tiles;
     const int tbase = block_exclusive_scan(nt, sh, total_tiles);
-    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j * BM);
+    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
     if (e < E && tot > 0) active[abase] = e;
@@ -408,10 +408,10 @@ __global__ __launch_bounds__(256) void route_finish_small(int T, int K, int E, i
     const int base = block_exclusive_scan(tot, sh, total_rows);
     if (e < E) { exp_off[e] = base; s_off[e] = base; }
     if (e == 0) exp_off[E] = total_rows;
-    const int nt = (e < E) ? (tot + BM - 1) / BM : 0;
+    const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
     int total_tiles;
     const int tbase = block_exclusive_scan(nt, sh, total_tiles);
-    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j * BM);
+    for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
     if (e < E && tot > 0) active[abase] = e;
