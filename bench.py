@@ -159,12 +159,25 @@ def main():
                  "algorithmic_bytes": int(gate_up_bytes), "algorithmic_flops": gate_up_flops,
                  "traffic": measured_traffic(w.name)})
 
+    # ---- per-kernel times (separate passes after the timed region) ----
+    kernel_ms = {"gate_up": round(gate_up_ms, 4)}
+    for name, kid in (("router_logits", bm.BEAM_KERNEL_ROUTER_LOGITS), ("down", bm.BEAM_KERNEL_DOWN),
+                      ("combine", bm.BEAM_KERNEL_COMBINE)):
+        n = min(K, 3)
+        kt = bm.KernelTimer(kid, n)
+        with kt:
+            for _ in range(n):
+                step()
+            torch.cuda.synchronize()
+        kernel_ms[name] = round(float(np.mean(kt.times_ms())), 4)
+
     # ---- whole-layer figures ----
     layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
     layer_wbytes = n_active * 3 * w.I * w.H * wbytes
     extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
              "layer_weight_gbs": round(layer_wbytes / (ms_per_step / 1e3) / 1e9, 1),
-             "distinct_experts": n_active, "ms_gpu_events": round(ms_gpu, 4), "ms_wall": round(ms_wall, 4)}
+             "distinct_experts": n_active, "ms_gpu_events": round(ms_gpu, 4), "ms_wall": round(ms_wall, 4),
+             "kernel_ms": kernel_ms}
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None

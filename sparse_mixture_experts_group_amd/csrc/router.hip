@@ -122,13 +122,13 @@ __global__ __launch_bounds__(256) void router_logits_reduce(int T, int E, const 
 // 16 x 16; each thread owns a (BT/16) x (BE/16) tile of outputs with two registers per
 // output: the running fma chain of the current chunk and the ordered sum of finished
 // chunks.  Tiles of HK hidden entries are staged through LDS (x transposed so a
-// thread's tokens are contiguous).
+// thread's tokens are contiguous).  H must be a multiple of HK = 64.
 template <bool XBF16, int BT, int BE>
 __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, const void* x,
                                                            const float* __restrict__ wr,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ z) {
-    constexpr int HK = 32;
+    constexpr int HK = 64;
     constexpr int TM = BT / 16, TN = BE / 16;
     constexpr int XP = BT + 4;               // padded LDS pitch of the transposed x tile
     __shared__ float xs[HK * XP];
@@ -150,28 +150,40 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
     const int xt = min(t0 + xr, T - 1);
     // w tile: HK rows x BE cols, float4 chunks
     constexpr int WV = HK * BE / 4 / 256;
-
+    // The global loads of tile h0 + HK are issued before the FMAs of tile h0 (register
+    // double buffering), so their latency overlaps the arithmetic.
+    float xv[XE];
+    f32x4 wv[WV];          // native vectors: kept in registers
+    int64_t xoff = static_cast<int64_t>(xt) * H + xc;
+    const float* wp = wr + e0;
+#pragma unroll
+    for (int i = 0; i < XE; ++i) xv[i] = load_act<XBF16>(x, xoff + i);
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+        const int c = tid + i * 256;
+        wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
+    }
     for (int h0 = 0; h0 < H; h0 += HK) {
-        float xv[XE];
-#pragma unroll
-        for (int i = 0; i < XE; ++i) xv[i] = load_act<XBF16>(x, static_cast<int64_t>(xt) * H + h0 + xc + i);
-        float4 wv[WV];
-#pragma unroll
-        for (int i = 0; i < WV; ++i) {
-            const int c = tid + i * 256;
-            const int k = c / (BE / 4), cc = (c % (BE / 4)) * 4;
-            wv[i] = *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(h0 + k) * E + e0 + cc);
-        }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < XE; ++i) xs[(xc + i) * XP + xr] = xv[i];
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int c = tid + i * 256;
-            const int k = c / (BE / 4), cc = (c % (BE / 4)) * 4;
-            *reinterpret_cast<float4*>(&ws[k * BE + cc]) = wv[i];
+            *reinterpret_cast<f32x4*>(&ws[(c / (BE / 4)) * BE + (c % (BE / 4)) * 4]) = wv[i];
         }
         __syncthreads();
+        if (h0 + HK < H) {
+            xoff += HK;
+            wp += static_cast<int64_t>(HK) * E;
+#pragma unroll
+            for (int i = 0; i < XE; ++i) xv[i] = load_act<XBF16>(x, xoff + i);
+#pragma unroll
+            for (int i = 0; i < WV; ++i) {
+                const int c = tid + i * 256;
+                wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
+            }
+        }
 #pragma unroll 4
         for (int k = 0; k < HK; ++k) {
             float a[TM], b[TN];
