@@ -77,7 +77,7 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
     L.z = take(sizeof(float) * T * E);
     // chunk sums of the small-T router kernel (only used below the tiled kernel's range)
-    L.zpart = take(router_uses_partials(T, static_cast<int>(E)) ? sizeof(float) * 64 * T * E : 0);
+    L.zpart = take(router_uses_partials(T, static_cast<int>(H), static_cast<int>(E)) ? sizeof(float) * 64 * T * E : 0);
     L.ids = take(sizeof(int32_t) * P);
     L.wts = take(sizeof(float) * P);
     L.blk_cnt = take(sizeof(int32_t) * L.nblk * E);

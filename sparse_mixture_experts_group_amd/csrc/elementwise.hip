@@ -10,6 +10,39 @@ namespace beam {
 // normalised router weights, which already carry the factor 2.5).  FP32 accumulation.
 // One block per token; 8 BF16 columns per thread per step.
 // ---------------------------------------------------------------------------
+// y[c .. c+7] of one token into acc: sum over i < K ascending of w_i * yperm[row_i, c ..],
+// FP32.  The loads of up to 8 picks are issued together, then their fmas.
+__device__ __forceinline__ void combine8(int H, int K, const uint16_t* __restrict__ yperm, const int32_t* s_row,
+                                         const float* s_w, int c, float* acc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int i0 = 0; i0 < K; i0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i0 + i < K) v[i] = *reinterpret_cast<const u32x4*>(yperm + static_cast<int64_t>(s_row[i0 + i]) * H + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i0 + i < K) {
+                const float wi = s_w[i0 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] = fmaf(wi, __uint_as_float(v[i][j] << 16), acc[2 * j]);
+                    acc[2 * j + 1] = fmaf(wi, __uint_as_float(v[i][j] & 0xFFFF0000u), acc[2 * j + 1]);
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* a) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = static_cast<uint32_t>(f32_to_bf16_bits(a[2 * j])) | (static_cast<uint32_t>(f32_to_bf16_bits(a[2 * j + 1])) << 16);
+    return o;
+}
+
 __global__ __launch_bounds__(256) void combine_bf16(int H, int K, const uint16_t* __restrict__ yperm,
                                                     const int32_t* __restrict__ row_of_pair,
                                                     const float* __restrict__ w,
@@ -23,22 +56,9 @@ __global__ __launch_bounds__(256) void combine_bf16(int H, int K, const uint16_t
     }
     __syncthreads();
     for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < K; ++i) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(yperm + static_cast<int64_t>(s_row[i]) * H + c);
-            const float wi = s_w[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] = fmaf(wi, __uint_as_float(v[j] << 16), acc[2 * j]);
-                acc[2 * j + 1] = fmaf(wi, __uint_as_float(v[j] & 0xFFFF0000u), acc[2 * j + 1]);
-            }
-        }
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j])) |
-                   (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j + 1])) << 16);
-        *reinterpret_cast<u32x4*>(y + t * H + c) = o;
+        float acc[8];
+        combine8(H, K, yperm, s_row, s_w, c, acc);
+        *reinterpret_cast<u32x4*>(y + t * H + c) = pack_bf16x8(acc);
     }
 }
 
@@ -79,18 +99,25 @@ __device__ __forceinline__ float prenorm_value(const uint16_t* row, const float*
     return v;
 }
 
+// The row is staged once in LDS with 16-byte loads (dynamic LDS: 4 rows of H BF16), so
+// the strided order of the sum of squares costs no narrow global loads and the output
+// passes do not re-read global memory.  H is a multiple of 8.
 __global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint16_t* __restrict__ h,
                                                     const float* __restrict__ gain, float eps,
                                                     float* __restrict__ xhat32, uint16_t* __restrict__ x16,
                                                     uint8_t* __restrict__ x8, float* __restrict__ xs) {
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    extern __shared__ uint16_t s_rows[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (t >= T) return;                       // no block barrier below: each wave owns its row
+    uint16_t* sr = s_rows + static_cast<int64_t>(wave) * H;
     const uint16_t* row = h + t * H;
+    for (int c = lane * 8; c < H; c += 512)
+        *reinterpret_cast<u32x4*>(sr + c) = *reinterpret_cast<const u32x4*>(row + c);
     float p = 0.0f;
     for (int c = lane; c < H; c += 64) {
-        const float v = bf16_bits_to_f32(row[c]);
+        const float v = bf16_bits_to_f32(sr[c]);
         p = __builtin_fmaf(v, v, p);
     }
 #pragma unroll
@@ -98,20 +125,29 @@ __global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint
     const float ms = __fdiv_rn(__shfl(p, 0, kWave), static_cast<float>(H));
     const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, eps)));
     float am = 0.0f;
-    for (int c = lane; c < H; c += 64) {
-        const float v = prenorm_value(row, gain, r, c);
-        if (xhat32) xhat32[t * H + c] = v;
-        if (x16) x16[t * H + c] = f32_to_bf16_bits(v);
-        am = fmaxf(am, fabsf(v));
+    for (int c = lane * 4; c < H; c += 256) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = prenorm_value(sr, gain, r, c + j);
+            am = fmaxf(am, fabsf(v[j]));
+        }
+        if (xhat32) *reinterpret_cast<f32x4*>(xhat32 + t * H + c) = f32x4{v[0], v[1], v[2], v[3]};
+        if (x16) {
+            u32x2 o;
+            o[0] = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+            o[1] = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+            *reinterpret_cast<u32x2*>(x16 + t * H + c) = o;
+        }
     }
     if (!x8) return;
     am = wave_max(am);
     const float sc = am > 0.0f ? am / 448.0f : 1.0f;
     const float inv = 1.0f / sc;
     for (int c = lane * 4; c < H; c += 256) {
-        const uint32_t q = f32x4_to_e4m3x4(prenorm_value(row, gain, r, c) * inv, prenorm_value(row, gain, r, c + 1) * inv,
-                                           prenorm_value(row, gain, r, c + 2) * inv,
-                                           prenorm_value(row, gain, r, c + 3) * inv);
+        const uint32_t q = f32x4_to_e4m3x4(prenorm_value(sr, gain, r, c) * inv, prenorm_value(sr, gain, r, c + 1) * inv,
+                                           prenorm_value(sr, gain, r, c + 2) * inv,
+                                           prenorm_value(sr, gain, r, c + 3) * inv);
         *reinterpret_cast<uint32_t*>(x8 + t * H + c) = q;
     }
     if (lane == 0) xs[t] = sc;
@@ -120,8 +156,14 @@ __global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint
 void launch_prenorm(hipStream_t st, int64_t T, int H, const uint16_t* h, const float* gain,
                     float eps, float* xhat32, uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale) {
     if (T == 0) return;
-    prenorm_rows<<<static_cast<unsigned>((T + 3) / 4), 256, 0, st>>>(T, H, h, gain, eps, xhat32, x_bf16, x_fp8,
-                                                                     x_scale);
+    static bool attr_set = false;     // up to 128 KB of LDS (H <= 16384): opt in once
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prenorm_rows),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 16384);
+        attr_set = true;
+    }
+    prenorm_rows<<<static_cast<unsigned>((T + 3) / 4), 256, 4 * sizeof(uint16_t) * H, st>>>(
+        T, H, h, gain, eps, xhat32, x_bf16, x_fp8, x_scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,7 +225,7 @@ void launch_quant_rows_fp8(hipStream_t st, int64_t rows, int cols, bool src_bf16
 // ---------------------------------------------------------------------------
 // combine + post-norm + constant-scale residual, one block per token (Beam overview,
 // "Residual stream": at step k the stream keeps sqrt((k-1)/k) of itself and adds
-// 1/sqrt(k) of the normalised sublayer output).  y stays in FP32 registers-by-LDS.
+// 1/sqrt(k) of the normalised sublayer output).  y stays in FP32 registers.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void post_residual(int H, int K, const uint16_t* __restrict__ yperm,
                                                      const int32_t* __restrict__ row_of_pair,
@@ -191,7 +233,7 @@ __global__ __launch_bounds__(256) void post_residual(int H, int K, const uint16_
                                                      const float* __restrict__ gain, float eps,
                                                      float c1, float c2, uint16_t* __restrict__ h,
                                                      uint16_t* __restrict__ moe_out) {
-    extern __shared__ float s_y[];            // H floats
+    constexpr int kPass = 8;                  // H <= 16384 = kPass * 256 threads * 8 columns
     __shared__ int32_t s_row[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
     __shared__ float s_red[4];
@@ -201,30 +243,16 @@ __global__ __launch_bounds__(256) void post_residual(int H, int K, const uint16_
         s_w[threadIdx.x] = w[t * K + threadIdx.x];
     }
     __syncthreads();
+    float y[kPass][8];                        // this thread's columns of y, FP32
     float ss = 0.0f;
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < K; ++i) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(yperm + static_cast<int64_t>(s_row[i]) * H + c);
-            const float wi = s_w[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] = fmaf(wi, __uint_as_float(v[j] << 16), acc[2 * j]);
-                acc[2 * j + 1] = fmaf(wi, __uint_as_float(v[j] & 0xFFFF0000u), acc[2 * j + 1]);
-            }
-        }
+    for (int p = 0; p < kPass; ++p) {
+        const int c = (p * 256 + static_cast<int>(threadIdx.x)) * 8;
+        if (c < H) {
+            combine8(H, K, yperm, s_row, s_w, c, y[p]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            s_y[c + j] = acc[j];
-            ss = fmaf(acc[j], acc[j], ss);
-        }
-        if (moe_out) {
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j])) |
-                       (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * j + 1])) << 16);
-            *reinterpret_cast<u32x4*>(moe_out + t * H + c) = o;
+            for (int j = 0; j < 8; ++j) ss = fmaf(y[p][j], y[p][j], ss);
+            if (moe_out) *reinterpret_cast<u32x4*>(moe_out + t * H + c) = pack_bf16x8(y[p]);
         }
     }
     ss = wave_sum(ss);
@@ -232,11 +260,21 @@ __global__ __launch_bounds__(256) void post_residual(int H, int K, const uint16_
     __syncthreads();
     const float tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
     const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-    for (int c = threadIdx.x; c < H; c += 256) {
-        float yn = s_y[c] * r;
-        if (gain) yn *= gain[c];
-        const float hv = bf16_bits_to_f32(h[t * H + c]);
-        h[t * H + c] = f32_to_bf16_bits(c1 * hv + c2 * yn);
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+        const int c = (p * 256 + static_cast<int>(threadIdx.x)) * 8;
+        if (c < H) {
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(h + t * H + c);
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float yn = y[p][j] * r;
+                if (gain) yn *= gain[c + j];
+                const float hj = __uint_as_float((j & 1) ? (hv[j >> 1] & 0xFFFF0000u) : (hv[j >> 1] << 16));
+                o[j] = c1 * hj + c2 * yn;
+            }
+            *reinterpret_cast<u32x4*>(h + t * H + c) = pack_bf16x8(o);
+        }
     }
 }
 
@@ -244,8 +282,8 @@ void launch_post_residual(hipStream_t st, int64_t T, int H, int K, const uint16_
                           const int32_t* row_of_pair, const float* w, const float* gain,
                           float eps, float c1, float c2, uint16_t* h, uint16_t* moe_out) {
     if (T == 0) return;
-    post_residual<<<static_cast<unsigned>(T), 256, sizeof(float) * H, st>>>(H, K, yperm, row_of_pair, w, gain, eps,
-                                                                             c1, c2, h, moe_out);
+    post_residual<<<static_cast<unsigned>(T), 256, 0, st>>>(H, K, yperm, row_of_pair, w, gain, eps, c1, c2, h,
+                                                             moe_out);
 }
 
 }  // namespace beam

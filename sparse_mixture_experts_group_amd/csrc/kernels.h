@@ -29,8 +29,11 @@ __host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
 constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
-// chunk sums) below this size, the register-tiled kernel above it.
-inline bool router_uses_partials(int64_t T, int E) { return !(E % 128 == 0 && T >= 256); }
+// chunk sums) below this size, the register-tiled kernel above it; the tiled kernel
+// stages whole multiples of 16 hidden entries of one chunk (H / 64 % 16 == 0).
+inline bool router_uses_partials(int64_t T, int H, int E) {
+    return !(E % 128 == 0 && T >= 256 && (H / 64) % 16 == 0);
+}
 
 inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
 

@@ -121,14 +121,15 @@ __global__ __launch_bounds__(256) void router_logits_reduce(int T, int E, const 
 // Large T: register-tiled kernel.  Block = BT tokens x BE experts, 256 threads as
 // 16 x 16; each thread owns a (BT/16) x (BE/16) tile of outputs with two registers per
 // output: the running fma chain of the current chunk and the ordered sum of finished
-// chunks.  Tiles of HK hidden entries are staged through LDS (x transposed so a
-// thread's tokens are contiguous).  H must be a multiple of HK = 64.
-template <bool XBF16, int BT, int BE>
+// chunks.  Tiles of HK hidden entries, HK dividing the chunk length H / 64, are staged
+// through LDS (x transposed so a thread's tokens are contiguous), so a chunk ends only
+// at a tile end and the fold is one uniform branch per tile.  The global loads of tile
+// h0 + HK are issued before the fmas of tile h0 (register double buffering).
+template <bool XBF16, int BT, int BE, int HK>
 __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, const void* x,
                                                            const float* __restrict__ wr,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ z) {
-    constexpr int HK = 64;
     constexpr int TM = BT / 16, TN = BE / 16;
     constexpr int XP = BT + 4;               // padded LDS pitch of the transposed x tile
     __shared__ float xs[HK * XP];
@@ -144,33 +145,37 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
 #pragma unroll
         for (int j = 0; j < TN; ++j) { acc[i][j] = 0.0f; tot[i][j] = 0.0f; }
 
-    // x tile: BT rows x HK cols = BT*HK/256 elements per thread (contiguous in h)
-    constexpr int XE = BT * HK / 256;
-    const int xr = tid / (HK / XE), xc = (tid % (HK / XE)) * XE;
-    const int xt = min(t0 + xr, T - 1);
-    // w tile: HK rows x BE cols, float4 chunks
-    constexpr int WV = HK * BE / 4 / 256;
-    // The global loads of tile h0 + HK are issued before the FMAs of tile h0 (register
-    // double buffering), so their latency overlaps the arithmetic.
+    // x tile: BT rows x HK cols, XE consecutive hidden entries per thread; w tile: HK rows
+    // x BE cols, WV float4 chunks per thread
+    constexpr int XE = (BT * HK + 255) / 256;
+    constexpr int XT = HK / XE;              // threads per x row
+    static_assert(HK % XE == 0 && BT * XT <= 256, "x tile mapping");
+    const int xr = tid / XT, xc = (tid % XT) * XE;
+    const bool xon = xr < BT;
+    const int xt = min(t0 + min(xr, BT - 1), T - 1);
+    constexpr int WV = (HK * BE / 4 + 255) / 256;
     float xv[XE];
     f32x4 wv[WV];          // native vectors: kept in registers
     int64_t xoff = static_cast<int64_t>(xt) * H + xc;
     const float* wp = wr + e0;
+    auto w_ok = [&](int i) { return (HK * BE / 4) % 256 == 0 || tid + i * 256 < HK * BE / 4; };
 #pragma unroll
     for (int i = 0; i < XE; ++i) xv[i] = load_act<XBF16>(x, xoff + i);
 #pragma unroll
     for (int i = 0; i < WV; ++i) {
         const int c = tid + i * 256;
-        wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
+        if (w_ok(i)) wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
     }
     for (int h0 = 0; h0 < H; h0 += HK) {
         __syncthreads();
+        if (xon) {
 #pragma unroll
-        for (int i = 0; i < XE; ++i) xs[(xc + i) * XP + xr] = xv[i];
+            for (int i = 0; i < XE; ++i) xs[(xc + i) * XP + xr] = xv[i];
+        }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int c = tid + i * 256;
-            *reinterpret_cast<f32x4*>(&ws[(c / (BE / 4)) * BE + (c % (BE / 4)) * 4]) = wv[i];
+            if (w_ok(i)) *reinterpret_cast<f32x4*>(&ws[(c / (BE / 4)) * BE + (c % (BE / 4)) * 4]) = wv[i];
         }
         __syncthreads();
         if (h0 + HK < H) {
@@ -181,10 +186,11 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
 #pragma unroll
             for (int i = 0; i < WV; ++i) {
                 const int c = tid + i * 256;
-                wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
+                if (w_ok(i))
+                    wv[i] = *reinterpret_cast<const f32x4*>(wp + static_cast<int64_t>(c / (BE / 4)) * E + (c % (BE / 4)) * 4);
             }
         }
-#pragma unroll 4
+#pragma unroll 8
         for (int k = 0; k < HK; ++k) {
             float a[TM], b[TN];
 #pragma unroll
@@ -195,12 +201,12 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-            if ((h0 + k + 1) % ch == 0) {          // chunk finished: fold it into the total
+        }
+        if ((h0 + HK) % ch == 0) {                 // chunk finished: fold it into the total
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) { tot[i][j] = __fadd_rn(tot[i][j], acc[i][j]); acc[i][j] = 0.0f; }
-            }
+                for (int j = 0; j < TN; ++j) { tot[i][j] = __fadd_rn(tot[i][j], acc[i][j]); acc[i][j] = 0.0f; }
         }
     }
 #pragma unroll
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(256) void route_scatter(int64_t npairs, int K, int 
 // ---------------------------------------------------------------------------
 void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
                           const float* wr, const float* bias, float* z, float* part) {
-    if (router_uses_partials(T, E)) {
+    if (router_uses_partials(T, H, E)) {
         dim3 grid((E + 63) / 64, 16, (T + 15) / 16);
         const size_t lds = sizeof(float) * 16 * 4 * (H / 64);
         if (x_bf16) router_logits_partial<true><<<grid, 256, lds, st>>>(T, H, E, x, wr, part);
@@ -474,14 +480,26 @@ void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, cons
         router_logits_reduce<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(T, E, part, bias, z);
         return;
     }
+    // tile depth: 80 (one whole Beam chunk), else 16; both divide the chunk length
+    const int ch = H / 64;
     if (T >= 16384) {
         dim3 grid((T + 63) / 64, E / 128);
-        if (x_bf16) router_logits_tiled<true, 64, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
-        else router_logits_tiled<false, 64, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        if (ch % 80 == 0) {
+            if (x_bf16) router_logits_tiled<true, 64, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 64, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        } else {
+            if (x_bf16) router_logits_tiled<true, 64, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 64, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        }
     } else {
         dim3 grid((T + 31) / 32, E / 128);
-        if (x_bf16) router_logits_tiled<true, 32, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
-        else router_logits_tiled<false, 32, 128><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        if (ch % 80 == 0) {
+            if (x_bf16) router_logits_tiled<true, 32, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 32, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        } else {
+            if (x_bf16) router_logits_tiled<true, 32, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 32, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+        }
     }
 }
 
