@@ -193,8 +193,10 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     g.meta = at<int32_t>(ws, L.meta);
     g.active = at<int32_t>(ws, L.active);
     g.max_tiles = L.max_tiles;
-    g.bm = L.bm;
     const int64_t P = T * c.topk;
+    // Few rows per expert (weight streaming): pairs of row tiles share an XCD's L2 slice
+    // with more column tiles; many rows (MFMA-bound): groups of 4 share weight panels.
+    g.group_m = (P >= 512LL * c.n_experts) ? 4 : 2;
     g.max_active = static_cast<int>(P < c.n_experts ? P : c.n_experts);
     return g;
 }

@@ -93,12 +93,9 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
 // each XCD has its own L2.  Logical block ids are dealt to XCDs in chunks of 32 (one
 // block per CU of an XCD), chunk c going to XCD c % 8, so the blocks one XCD runs at a
 // time are 32 consecutive logical ids.  Logical ids walk groups of `group_m` row tiles
-// across all column tiles, column-major inside a group.  group_m = 4 (256-row tiles,
-// MFMA-bound): 32 consecutive ids cover 4 row tiles x 8 column tiles, so A tiles and
-// weight panels are both shared inside an XCD.  group_m = 1 (128-row tiles, bound by
-// streaming weights): consecutive ids are the column tiles of one row tile, so that
-// expert's gathered activation tile stays in the XCD's L2 while its weight panels
-// stream past.  The grid is a multiple of 256 blocks.
+// across all column tiles, column-major inside a group: 32 consecutive ids cover
+// group_m row tiles x 32/group_m column tiles, so activation tiles and weight panels
+// are both shared inside an XCD.  The grid covers whole groups in whole chunks of 256.
 __device__ __forceinline__ void prefill_tile_of_block(int n_tiles_n, int group_m, int& tile, int& nt) {
     const int i = blockIdx.x;
     const int xcd = i & 7, k = i >> 3;

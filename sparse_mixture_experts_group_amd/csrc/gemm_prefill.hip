@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
     const int n_tiles_n = g.n_out / NCOL;
     int tile, nt;
-    prefill_tile_of_block(n_tiles_n, 4, tile, nt);
+    prefill_tile_of_block(n_tiles_n, g.group_m, tile, nt);
     if (tile >= g.meta[kMetaTiles]) return;
     const int2 ti = g.tiles[tile];                     // (expert, tile of the expert)
     const int e = ti.x, n_e = g.exp_cnt[e];
@@ -308,7 +308,9 @@ static void launch_prefill_dtype(hipStream_t st, GemmMode mode, const GroupedGem
 void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8) {
     if (g.max_tiles == 0) return;
     const int ncol = (mode == kGateUp) ? 128 : 256;
-    const int blocks = (g.max_tiles * (g.n_out / ncol) + 255) / 256 * 256;   // whole XCD chunks
+    // every (row tile, column tile) of whole groups of group_m row tiles, in whole XCD chunks
+    const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
+    const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
     if (fp8) launch_prefill_dtype<true>(st, mode, g, blocks);
     else launch_prefill_dtype<false>(st, mode, g, blocks);
 }

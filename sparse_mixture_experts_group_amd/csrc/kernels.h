@@ -75,7 +75,7 @@ struct GroupedGemmArgs {
     const int32_t* meta;      // meta[kMetaTiles], meta[kMetaActive]
     const int32_t* active;    // [E] experts with rows, ascending
     int max_tiles;            // grid bound for tile-driven kernels
-    int bm;                   // rows per tile of the tile list (prefill kernels)
+    int group_m;              // prefill block order: row tiles per XCD group (2 or 4)
     int max_active;           // grid bound for expert-driven kernels
     void* out;                // [rows, n_out]
     int64_t ldo;              // elements per output row
