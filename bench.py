@@ -1,6 +1,7 @@
 """Benchmark of the Beam MoE layer on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+python bench.py --workload NAME --sweep 16,64,256,... [--steps K]   (one line per T)
 
 A step is one full `beam_moe_forward` (router, permutation, gate/up GEMM with SwiGLU,
 down GEMM, combine) -- or `beam_moe_sublayer_forward` for the sublayer workload -- over
@@ -42,6 +43,9 @@ def parse():
     p.add_argument("--workload", default="beam_decode_t16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    p.add_argument("--sweep", default="", metavar="T1,T2,...",
+                   help="time the workload's layer at each token count (prefixes of its tokens); "
+                        "one JSON line per count")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 3 plain device copies of MIB MiB (reference for HBM byte counters)")
     return p.parse_args()
@@ -62,87 +66,98 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this layer is built and timed on a single MI355X; "
-              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import sparse_mixture_experts_group_amd as bm
-    from beam_inputs import WORKLOADS, make_inputs, DT_BF16, DT_FP8, DT_F32, DTYPE_NAMES
+class Layer:
+    """Device copies of one workload's weights (inputs resident in HBM) and a step
+    function for any token count up to the workload's T."""
 
-    w = WORKLOADS[args.workload]
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    t0 = time.time()
-    log(f"[bench] generating inputs for {w.name} (T={w.T}) ...")
-    inp = make_inputs(w)
-    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+    def __init__(self, w, inp):
+        import torch
+        import sparse_mixture_experts_group_amd as bm
+        self.bm, self.w, self.inp = bm, w, inp
+        self.dev = dev = torch.device("cuda:0")
 
-    def up(a, dt=None):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
 
-    x = up(inp.x)
-    wr = up(inp.w_router)
-    w13, w2 = up(inp.w13), up(inp.w2)
-    s13 = up(inp.w13_scale) if inp.w13_scale is not None else None
-    s2 = up(inp.w2_scale) if inp.w2_scale is not None else None
-    bias = up(inp.logit_bias) if inp.logit_bias is not None else None
-    cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg, topk=w.K,
-                         routed_scale=w.alpha, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
-                         fp8_block=w.fp8_block, norm_eps=w.norm_eps)
-    ws = bm.alloc_workspace(cfg, w.T, dev)
-    ids = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
-    wts = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
-    y = torch.empty_like(x)
-    h = x.clone()      # the sublayer updates the residual stream in place, step after step
+        self.x_all = up(inp.x)
+        self.wr = up(inp.w_router)
+        self.w13, self.w2 = up(inp.w13), up(inp.w2)
+        self.s13 = up(inp.w13_scale) if inp.w13_scale is not None else None
+        self.s2 = up(inp.w2_scale) if inp.w2_scale is not None else None
+        self.bias = up(inp.logit_bias) if inp.logit_bias is not None else None
+        self.cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg,
+                                  topk=w.K, routed_scale=w.alpha, act_dtype=w.act_dtype,
+                                  weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
 
-    def step():
-        if w.sublayer:
-            bm.beam_moe_sublayer_forward(cfg, h, w.step_k, wr, w13, w2, logit_bias=bias, w13_scale=s13,
-                                         w2_scale=s2, ids=ids, weights=wts, ws=ws)
-        else:
-            bm.beam_moe_forward(cfg, x, wr, w13, w2, logit_bias=bias, w13_scale=s13, w2_scale=s2, y=y, ids=ids,
-                                weights=wts, ws=ws)
+    def measure(self, T: int, steps: int, warmup: int) -> dict:
+        """Time `steps` forwards over the first T tokens (after `warmup` untimed ones):
+        step time from HIP events and the wall clock, the gate/up GEMM's duration from
+        events the library records around it, then the other kernels in separate passes."""
+        import torch
+        bm, w = self.bm, self.w
+        x = self.x_all[:T].contiguous()
+        ws = bm.alloc_workspace(self.cfg, T, self.dev)
+        ids = torch.empty((T, w.K), dtype=torch.int32, device=self.dev)
+        wts = torch.empty((T, w.K), dtype=torch.float32, device=self.dev)
+        y = torch.empty_like(x)
+        h = x.clone()      # the sublayer updates the residual stream in place, step after step
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    K = args.steps
-    timer = bm.KernelTimer(bm.BEAM_KERNEL_GATE_UP, K)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    with timer:
-        ev0.record()
-        for _ in range(K):
+        def step():
+            if w.sublayer:
+                bm.beam_moe_sublayer_forward(self.cfg, h, w.step_k, self.wr, self.w13, self.w2,
+                                             logit_bias=self.bias, w13_scale=self.s13, w2_scale=self.s2,
+                                             ids=ids, weights=wts, ws=ws)
+            else:
+                bm.beam_moe_forward(self.cfg, x, self.wr, self.w13, self.w2, logit_bias=self.bias,
+                                    w13_scale=self.s13, w2_scale=self.s2, y=y, ids=ids, weights=wts, ws=ws)
+
+        for _ in range(warmup):
             step()
-        ev1.record()
         torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    ms_gpu = ev0.elapsed_time(ev1) / K
-    ms_wall = (wall1 - wall0) * 1e3 / K
-    ms_per_step = max(ms_gpu, ms_wall)
-    gate_up_ms = float(np.mean(timer.times_ms()))
-    tokens_per_s = w.T / (ms_per_step / 1e3)
+        timer = bm.KernelTimer(bm.BEAM_KERNEL_GATE_UP, steps)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        with timer:
+            ev0.record()
+            for _ in range(steps):
+                step()
+            ev1.record()
+            torch.cuda.synchronize()
+        wall1 = time.perf_counter()
+        ms_gpu = ev0.elapsed_time(ev1) / steps
+        ms_wall = (wall1 - wall0) * 1e3 / steps
+        kernel_ms = {"gate_up": round(float(np.mean(timer.times_ms())), 4)}
+        # per-kernel times (separate passes after the timed region)
+        for name, kid in (("router_logits", bm.BEAM_KERNEL_ROUTER_LOGITS), ("down", bm.BEAM_KERNEL_DOWN),
+                          ("combine", bm.BEAM_KERNEL_COMBINE)):
+            n = min(steps, 3)
+            kt = bm.KernelTimer(kid, n)
+            with kt:
+                for _ in range(n):
+                    step()
+                torch.cuda.synchronize()
+            kernel_ms[name] = round(float(np.mean(kt.times_ms())), 4)
+        ids_np = ids.cpu().numpy()
+        return {"ms_gpu": ms_gpu, "ms_wall": ms_wall, "ms_per_step": max(ms_gpu, ms_wall),
+                "kernel_ms": kernel_ms, "n_active": int(np.unique(ids_np).size),
+                "max_rows": int(np.bincount(ids_np.reshape(-1), minlength=w.E).max())}
 
-    # ---- roofline of the dominant kernel (grouped gate/up GEMM) ----
-    ids_np = ids.cpu().numpy()
-    n_active = int(np.unique(ids_np).size)
-    P = w.T * w.K
+
+def gate_up_roofline(w, T: int, n_active: int, gate_up_ms: float) -> dict:
+    """Roofline of the grouped gate/up GEMM: algorithmic bytes (routed experts' gate/up
+    weights, scales, x, the SwiGLU output) and flops per launch over its duration; the
+    bound is whichever of the HBM and MFMA times is larger."""
+    from beam_inputs import DT_BF16, DT_FP8, DT_F32
+    P = T * w.K
     wbytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[w.weight_dtype]
-    abytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[w.weight_dtype]
     gate_up_weight_bytes = n_active * 2 * w.I * w.H * wbytes
     if w.weight_dtype == DT_FP8:
         gate_up_weight_bytes += n_active * (2 * w.I // 128) * (w.H // 128) * 4
-    gate_up_bytes = gate_up_weight_bytes + w.T * w.H * abytes + P * w.I * 2
+    gate_up_bytes = gate_up_weight_bytes + T * w.H * wbytes + P * w.I * 2
     gate_up_flops = 2.0 * P * w.H * 2 * w.I
     peak_tf = MFMA_PEAK_TFLOPS[w.weight_dtype]
     t_hbm = gate_up_bytes / (HBM_PEAK_GBS * 1e9)
@@ -156,28 +171,64 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_tf, 4)}
     roof.update({"kernel": "grouped gate/up GEMM + SwiGLU", "kernel_ms": round(gate_up_ms, 4),
-                 "algorithmic_bytes": int(gate_up_bytes), "algorithmic_flops": gate_up_flops,
-                 "traffic": measured_traffic(w.name)})
+                 "algorithmic_bytes": int(gate_up_bytes), "algorithmic_flops": gate_up_flops})
+    return roof
 
-    # ---- per-kernel times (separate passes after the timed region) ----
-    kernel_ms = {"gate_up": round(gate_up_ms, 4)}
-    for name, kid in (("router_logits", bm.BEAM_KERNEL_ROUTER_LOGITS), ("down", bm.BEAM_KERNEL_DOWN),
-                      ("combine", bm.BEAM_KERNEL_COMBINE)):
-        n = min(K, 3)
-        kt = bm.KernelTimer(kid, n)
-        with kt:
-            for _ in range(n):
-                step()
-            torch.cuda.synchronize()
-        kernel_ms[name] = round(float(np.mean(kt.times_ms())), 4)
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer is built and timed on a single MI355X; "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from beam_inputs import WORKLOADS, make_inputs, DT_F32, DTYPE_NAMES
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    if args.sweep:
+        ts = [int(t) for t in args.sweep.split(",")]
+        w = w.with_T(max(ts))
+    t0 = time.time()
+    log(f"[bench] generating inputs for {w.name} (T={w.T}) ...")
+    inp = make_inputs(w)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+    layer = Layer(w, inp)
+
+    if args.sweep:
+        # one JSON line per token count (batch sizes between decode and prefill)
+        for T in ts:
+            r = layer.measure(T, args.steps, args.warmup)
+            roof = gate_up_roofline(w, T, r["n_active"], r["kernel_ms"]["gate_up"])
+            wbytes = {0: 4, 1: 2, 2: 1}[w.weight_dtype]
+            layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
+            print(json.dumps({"sweep": w.name, "T": T, "ms_per_step": round(r["ms_per_step"], 4),
+                              "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1),
+                              "distinct_experts": r["n_active"], "max_rows_per_expert": r["max_rows"],
+                              "layer_weight_gbs": round(layer_wbytes / (r["ms_per_step"] / 1e3) / 1e9, 1),
+                              "gate_up_roofline": {k: roof[k] for k in ("bound", "achieved", "unit", "frac")},
+                              "kernel_ms": r["kernel_ms"]}), flush=True)
+        return
+
+    K = args.steps
+    r = layer.measure(w.T, K, args.warmup)
+    ms_per_step = r["ms_per_step"]
+    tokens_per_s = w.T / (ms_per_step / 1e3)
+    roof = gate_up_roofline(w, w.T, r["n_active"], r["kernel_ms"]["gate_up"])
+    roof["traffic"] = measured_traffic(w.name)
 
     # ---- whole-layer figures ----
+    P = w.T * w.K
+    wbytes = {0: 4, 1: 2, 2: 1}[w.weight_dtype]
     layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
-    layer_wbytes = n_active * 3 * w.I * w.H * wbytes
+    layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
     extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
              "layer_weight_gbs": round(layer_wbytes / (ms_per_step / 1e3) / 1e9, 1),
-             "distinct_experts": n_active, "ms_gpu_events": round(ms_gpu, 4), "ms_wall": round(ms_wall, 4),
-             "kernel_ms": kernel_ms}
+             "distinct_experts": r["n_active"], "ms_gpu_events": round(r["ms_gpu"], 4),
+             "ms_wall": round(r["ms_wall"], 4), "kernel_ms": r["kernel_ms"]}
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None

@@ -198,6 +198,7 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     // with more column tiles; many rows (MFMA-bound): groups of 4 share weight panels.
     g.group_m = (P >= 512LL * c.n_experts) ? 4 : 2;
     g.max_active = static_cast<int>(P < c.n_experts ? P : c.n_experts);
+    g.max_rows = static_cast<int>(T);     // a token picks an expert at most once
     return g;
 }
 

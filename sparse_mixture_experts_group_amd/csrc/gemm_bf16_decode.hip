@@ -10,8 +10,8 @@
 //
 // One block per (active expert, 64 output columns); each wave streams 16 weight rows
 // (32 for gate/up) straight from HBM into MFMA B operands with deep unrolling, and the
-// expert's activation rows ride along as the A operand, 16 at a time (rows beyond the
-// expert's count issue no loads).  v_mfma_f32_16x16x32_bf16.
+// expert's activation rows ride along as the A operand, 16 or 32 at a time (rows beyond
+// the expert's count issue no loads).  v_mfma_f32_16x16x32_bf16.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -22,7 +22,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // ---------------------------------------------------------------------------
 // decode: weight streaming
 // ---------------------------------------------------------------------------
-template <int MODE, bool GATHER, int U>
+template <int MODE, bool GATHER, int U, int R>
 __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
     const int slot = blockIdx.y;
     if (slot >= g.meta[kMetaActive]) return;
@@ -38,15 +38,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
     const uint16_t* wu = wp + static_cast<int64_t>(g.n_out) * g.kd;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 
-    for (int m0 = 0; m0 < rows; m0 += 16) {
-        const int m = m0 + ln;
-        const bool mv = m < rows;
-        const int mr = mv ? m : rows - 1;
-        const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
-        const uint16_t* ap = static_cast<const uint16_t*>(g.a) + arow * g.lda + lq * 8;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up
+    // to 16 R rows stream their weights once.
+    for (int m0 = 0; m0 < rows; m0 += 16 * R) {
+        bool mv[R];
+        const uint16_t* ap[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = m0 + 16 * r + ln;
+            mv[r] = m < rows;
+            const int mr = mv[r] ? m : rows - 1;
+            const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
+            ap[r] = static_cast<const uint16_t*>(g.a) + arow * g.lda + lq * 8;
+        }
+        f32x4 acc0[R], acc1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
         for (int k = 0; k < g.kd; k += 32 * U) {
-            u32x4 b0[U], b1[U], a[U];
+            u32x4 b0[U], b1[U], a[R][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) b0[u] = *reinterpret_cast<const u32x4*>(wp + k + u * 32);
             if (MODE == kGateUp) {
@@ -54,25 +63,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
                 for (int u = 0; u < U; ++u) b1[u] = *reinterpret_cast<const u32x4*>(wu + k + u * 32);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                a[u] = u32x4{0u, 0u, 0u, 0u};
-                if (mv) a[u] = *reinterpret_cast<const u32x4*>(ap + k + u * 32);
-            }
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b0[u]), acc0, 0, 0, 0);
-                if (MODE == kGateUp)
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b1[u]), acc1, 0, 0, 0);
-            }
-        }
-        // C[m = lq*4 + i][n = ln]
+                for (int u = 0; u < U; ++u) {
+                    a[r][u] = u32x4{0u, 0u, 0u, 0u};
+                    if (mv[r]) a[r][u] = *reinterpret_cast<const u32x4*>(ap[r] + k + u * 32);
+                }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mm = m0 + lq * 4 + i;
-            if (mm >= rows) continue;
-            const float v = (MODE == kGateUp) ? silu(acc0[i]) * acc1[i] : acc0[i];
-            out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    acc0[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r][u]), as_bf16x8(b0[u]), acc0[r], 0, 0, 0);
+                    if (MODE == kGateUp)
+                        acc1[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r][u]), as_bf16x8(b1[u]), acc1[r], 0, 0, 0);
+                }
         }
+        // C[m = lq*4 + i][n = ln] of row tile r
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mm = m0 + 16 * r + lq * 4 + i;
+                if (mm >= rows) continue;
+                const float v = (MODE == kGateUp) ? silu(acc0[r][i]) * acc1[r][i] : acc0[r][i];
+                out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
+            }
     }
 }
 
@@ -80,7 +95,10 @@ void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArg
     if (g.max_active == 0) return;
     dim3 grid((g.n_out + 63) / 64, g.max_active);
     const bool u8 = (g.kd % 256) == 0;
-#define BEAM_DEC(M, GA, U) gemm_bf16_decode<M, GA, U><<<grid, 256, 0, st>>>(g)
+    const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
+#define BEAM_DEC(M, GA, U) \
+    do { if (r2) gemm_bf16_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
+         else gemm_bf16_decode<M, GA, U, 1><<<grid, 256, 0, st>>>(g); } while (0)
     if (mode == kGateUp) {
         if (g.gather) { if (u8) BEAM_DEC(kGateUp, true, 8); else BEAM_DEC(kGateUp, true, 1); }
         else          { if (u8) BEAM_DEC(kGateUp, false, 8); else BEAM_DEC(kGateUp, false, 1); }

@@ -31,9 +31,9 @@ __device__ __forceinline__ f32x4 mfma16_fp8(i32x8 a, i32x8 b) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// decode: weight streaming, 16 rows x 16 columns per wave
+// decode: weight streaming, 16 columns per wave, 16 or 32 rows per pass
 // ---------------------------------------------------------------------------
-template <int MODE, bool GATHER, int U>
+template <int MODE, bool GATHER, int U, int R>
 __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
     const int slot = blockIdx.y;
     if (slot >= g.meta[kMetaActive]) return;
@@ -51,15 +51,24 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
     const float* swu = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + n0) / 128) * kb_n;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 
-    for (int m0 = 0; m0 < rows; m0 += 16) {
-        const int m = m0 + ln;
-        const bool mv = m < rows;
-        const int mr = mv ? m : rows - 1;
-        const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
-        const uint8_t* ap = static_cast<const uint8_t*>(g.a) + arow * g.lda + lq * 32;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up
+    // to 16 R rows stream their weights once.
+    for (int m0 = 0; m0 < rows; m0 += 16 * R) {
+        bool mv[R];
+        const uint8_t* ap[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = m0 + 16 * r + ln;
+            mv[r] = m < rows;
+            const int mr = mv[r] ? m : rows - 1;
+            const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
+            ap[r] = static_cast<const uint8_t*>(g.a) + arow * g.lda + lq * 32;
+        }
+        f32x4 acc0[R], acc1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
         for (int k = 0; k < g.kd; k += 128 * U) {
-            u32x4 b0[U][2], b1[U][2], a[U][2];
+            u32x4 b0[U][2], b1[U][2], a[R][U][2];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 b0[u][0] = *reinterpret_cast<const u32x4*>(wp + k + u * 128);
@@ -73,39 +82,46 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                a[u][0] = u32x4{0u, 0u, 0u, 0u};
-                a[u][1] = u32x4{0u, 0u, 0u, 0u};
-                if (mv) {
-                    a[u][0] = *reinterpret_cast<const u32x4*>(ap + k + u * 128);
-                    a[u][1] = *reinterpret_cast<const u32x4*>(ap + k + u * 128 + 16);
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    a[r][u][0] = u32x4{0u, 0u, 0u, 0u};
+                    a[r][u][1] = u32x4{0u, 0u, 0u, 0u};
+                    if (mv[r]) {
+                        a[r][u][0] = *reinterpret_cast<const u32x4*>(ap[r] + k + u * 128);
+                        a[r][u][1] = *reinterpret_cast<const u32x4*>(ap[r] + k + u * 128 + 16);
+                    }
                 }
-            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int kb = k / 128 + u;
-                const i32x8 av = join(a[u][0], a[u][1]);
-                const f32x4 t0 = mfma16_fp8(av, join(b0[u][0], b0[u][1]));
                 const float s0 = swg[kb];
+                const float s1 = (MODE == kGateUp) ? swu[kb] : 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc0[i] = fmaf(t0[i], s0, acc0[i]);
-                if (MODE == kGateUp) {
-                    const f32x4 t1 = mfma16_fp8(av, join(b1[u][0], b1[u][1]));
-                    const float s1 = swu[kb];
+                for (int r = 0; r < R; ++r) {
+                    const i32x8 av = join(a[r][u][0], a[r][u][1]);
+                    const f32x4 t0 = mfma16_fp8(av, join(b0[u][0], b0[u][1]));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc1[i] = fmaf(t1[i], s1, acc1[i]);
+                    for (int i = 0; i < 4; ++i) acc0[r][i] = fmaf(t0[i], s0, acc0[r][i]);
+                    if (MODE == kGateUp) {
+                        const f32x4 t1 = mfma16_fp8(av, join(b1[u][0], b1[u][1]));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc1[r][i] = fmaf(t1[i], s1, acc1[r][i]);
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mm = m0 + lq * 4 + i;
-            if (mm >= rows) continue;
-            const int64_t ar = GATHER ? g.pair_of_row[row0 + mm] / g.topk : static_cast<int64_t>(row0 + mm);
-            const float sa = g.a_scale[ar];
-            const float v = (MODE == kGateUp) ? silu(acc0[i] * sa) * (acc1[i] * sa) : acc0[i] * sa;
-            out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
-        }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mm = m0 + 16 * r + lq * 4 + i;
+                if (mm >= rows) continue;
+                const int64_t ar = GATHER ? g.pair_of_row[row0 + mm] / g.topk : static_cast<int64_t>(row0 + mm);
+                const float sa = g.a_scale[ar];
+                const float v = (MODE == kGateUp) ? silu(acc0[r][i] * sa) * (acc1[r][i] * sa) : acc0[r][i] * sa;
+                out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
+            }
     }
 }
 
@@ -113,7 +129,10 @@ void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs
     if (g.max_active == 0) return;
     dim3 grid((g.n_out + 63) / 64, g.max_active);
     const bool u4 = (g.kd % 512) == 0;
-#define BEAM_DEC(M, GA, U) gemm_fp8_decode<M, GA, U><<<grid, 256, 0, st>>>(g)
+    const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
+#define BEAM_DEC(M, GA, U) \
+    do { if (r2) gemm_fp8_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
+         else gemm_fp8_decode<M, GA, U, 1><<<grid, 256, 0, st>>>(g); } while (0)
     if (mode == kGateUp) {
         if (g.gather) { if (u4) BEAM_DEC(kGateUp, true, 4); else BEAM_DEC(kGateUp, true, 1); }
         else          { if (u4) BEAM_DEC(kGateUp, false, 4); else BEAM_DEC(kGateUp, false, 1); }

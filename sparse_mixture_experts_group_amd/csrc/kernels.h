@@ -26,13 +26,14 @@ __host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
     const int64_t m = (n + 31) / 32;
     return static_cast<int>((j * m / nt) * 32);
 }
-constexpr int kDecodeMaxT = 32;     // token counts up to this use the streaming GEMMs
+constexpr int kDecodeMaxT = 256;    // token counts up to this use the streaming GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
-// chunk sums) below this size, the register-tiled kernel above it; the tiled kernel
-// stages whole multiples of 16 hidden entries of one chunk (H / 64 % 16 == 0).
+// chunk sums) below 4096 tokens, where it fills the chip and the tiled kernel cannot,
+// and the register-tiled kernel from there on; the tiled kernel stages whole multiples
+// of 16 hidden entries of one chunk (H / 64 % 16 == 0).
 inline bool router_uses_partials(int64_t T, int H, int E) {
-    return !(E % 128 == 0 && T >= 256 && (H / 64) % 16 == 0);
+    return !(E % 128 == 0 && T >= 4096 && (H / 64) % 16 == 0);
 }
 
 inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
@@ -77,6 +78,7 @@ struct GroupedGemmArgs {
     int max_tiles;            // grid bound for tile-driven kernels
     int group_m;              // prefill block order: row tiles per XCD group (2 or 4)
     int max_active;           // grid bound for expert-driven kernels
+    int max_rows;             // bound on the rows of one expert (min(T, T*K))
     void* out;                // [rows, n_out]
     int64_t ldo;              // elements per output row
 };

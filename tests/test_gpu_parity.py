@@ -148,7 +148,10 @@ def test_router_all_ties_and_duplicated_columns():
 # Beam-shaped BF16 layer
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,T", [("beam_decode_t16", None), ("beam_decode_t16", 1),
-                                    ("beam_decode_t16", 17), ("beam_prefill_t4096", None),
+                                    ("beam_decode_t16", 17), ("beam_decode_t16", 32),
+                                    ("beam_prefill_t4096", 33), ("beam_prefill_t4096", 256),
+                                    ("beam_prefill_t4096", 257), ("beam_prefill_t4096", 1000),
+                                    ("beam_prefill_t4096", None),
                                     ("beam_prefill_t4096", 4097), ("beam_skewed_t32768", None)])
 def test_beam_bf16_layer(name, T):
     w, full, dev, x, bias = gpu_inputs(name, T)
@@ -163,8 +166,8 @@ def test_beam_bf16_layer(name, T):
     zg = ws_region(ws, m["logits"], w.T * w.E, np.float32).reshape(w.T, w.E)
     assert np.array_equal(zg, z)
     check_permutation(w, ws, ids)
-    # layer output on sampled tokens (all tokens for the decode batch)
-    tok = np.arange(w.T) if w.T <= 32 else sample_tokens(w.T)
+    # layer output of every token up to T = 300 (every tile of the grid), else sampled
+    tok = np.arange(w.T) if w.T <= 300 else sample_tokens(w.T)
     yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
     yg = y.float().cpu().numpy()[tok].astype(np.float64)
     err = rel_inf(yg, yref)
@@ -224,20 +227,24 @@ def test_fp8_sublayer():
     assert e_h <= TOL[DT_FP8]
 
 
-def test_fp8_forward_decode():
-    """FP8 experts on the decode-sized batch (streaming kernels) against the oracle."""
+@pytest.mark.parametrize("T", [16, 200, 700])
+def test_fp8_forward(T):
+    """FP8 experts through beam_moe_forward: the streaming kernels (T <= 256; 16 or 32
+    rows per pass) and the LDS-tiled kernels with mostly partial tiles (T = 700)."""
     w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192")
     from dataclasses import replace
     from beam_inputs import token_inputs, to_bf16_bits
-    w = replace(w0, T=16, sublayer=False, x_recipe="rms_normal")
+    w = replace(w0, T=T, sublayer=False, x_recipe="rms_normal")
     x = to_bf16_bits(token_inputs(w))
-    print("[case] fp8 forward T=16", flush=True)
+    print(f"[case] fp8 forward T={T}", flush=True)
     cfg, y, ids, wts, ws = run_forward(w, dev, x, None)
     x32 = oracle.bf16_to_f32(x)
     z = oracle.router_logits(x32, full.w_router, None)
     rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
     check_routing(w, ids, wts, rid, rw)
-    yref = oracle.moe_combine(x32.astype(np.float64), rid, rw, bank_of(w, full))
-    err = rel_inf(y.float().cpu().numpy().astype(np.float64), yref)
-    print(f"[case] fp8 forward T=16 rel_inf={err:.3e}", flush=True)
+    check_permutation(w, ws, ids)
+    tok = np.arange(T) if T <= 300 else sample_tokens(T)
+    yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
+    err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
+    print(f"[case] fp8 forward T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[DT_FP8]
