@@ -8,10 +8,11 @@
 // Rows r are the token->expert pairs sorted by expert, so each expert's rows are one
 // contiguous range [exp_off[e], exp_off[e] + exp_cnt[e]).
 //
-// One block per (active expert, 64 output columns); each wave streams 16 weight rows
-// (32 for gate/up) straight from HBM into MFMA B operands with deep unrolling, and the
-// expert's activation rows ride along as the A operand, 16 or 32 at a time (rows beyond
-// the expert's count issue no loads).  v_mfma_f32_16x16x32_bf16.
+// One block per (active expert, 64 output columns for gate/up, 128 for down); each wave
+// streams 32 weight rows (16 gate + 16 up, or 32 down rows) straight from HBM into MFMA
+// B operands with deep unrolling, and the expert's activation rows ride along as the A
+// operand, 16 or 32 at a time (rows beyond the expert's count issue no loads).
+// v_mfma_f32_16x16x32_bf16.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -29,13 +30,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
     const int e = g.active[slot];
     const int rows = g.exp_cnt[e], row0 = g.exp_off[e];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * 4 + wave) * 16;
+    // gate/up: 16 output columns per wave, streams of their gate and up rows; down: 32
+    // output columns per wave as two streams of 16 rows
+    constexpr int WC = (MODE == kGateUp) ? 16 : 32;
+    const int n0 = (blockIdx.x * 4 + wave) * WC;
     if (n0 >= g.n_out) return;
     const int ln = lane & 15, lq = lane >> 4;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const uint16_t* wp = static_cast<const uint16_t*>(g.w) +
                          (static_cast<int64_t>(e) * nw + n0 + ln) * g.kd + lq * 8;
-    const uint16_t* wu = wp + static_cast<int64_t>(g.n_out) * g.kd;
+    const uint16_t* wu = wp + static_cast<int64_t>(MODE == kGateUp ? g.n_out : 16) * g.kd;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 
     // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up
@@ -58,10 +62,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
             u32x4 b0[U], b1[U], a[R][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) b0[u] = *reinterpret_cast<const u32x4*>(wp + k + u * 32);
-            if (MODE == kGateUp) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) b1[u] = *reinterpret_cast<const u32x4*>(wu + k + u * 32);
-            }
+            for (int u = 0; u < U; ++u) b1[u] = *reinterpret_cast<const u32x4*>(wu + k + u * 32);
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -74,8 +76,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     acc0[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r][u]), as_bf16x8(b0[u]), acc0[r], 0, 0, 0);
-                    if (MODE == kGateUp)
-                        acc1[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r][u]), as_bf16x8(b1[u]), acc1[r], 0, 0, 0);
+                    acc1[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r][u]), as_bf16x8(b1[u]), acc1[r], 0, 0, 0);
                 }
         }
         // C[m = lq*4 + i][n = ln] of row tile r
@@ -85,15 +86,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
             for (int i = 0; i < 4; ++i) {
                 const int mm = m0 + 16 * r + lq * 4 + i;
                 if (mm >= rows) continue;
-                const float v = (MODE == kGateUp) ? silu(acc0[r][i]) * acc1[r][i] : acc0[r][i];
-                out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
+                uint16_t* orow = out + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
+                if (MODE == kGateUp) {
+                    orow[0] = f32_to_bf16_bits(silu(acc0[r][i]) * acc1[r][i]);
+                } else {
+                    orow[0] = f32_to_bf16_bits(acc0[r][i]);
+                    orow[16] = f32_to_bf16_bits(acc1[r][i]);
+                }
             }
     }
 }
 
 void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
     if (g.max_active == 0) return;
-    dim3 grid((g.n_out + 63) / 64, g.max_active);
+    const int cols_per_block = (mode == kGateUp) ? 64 : 128;     // n_out is a multiple of 32
+    dim3 grid((g.n_out + cols_per_block - 1) / cols_per_block, g.max_active);
     const bool u8 = (g.kd % 256) == 0;
     const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
 #define BEAM_DEC(M, GA, U) \
