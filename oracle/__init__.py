@@ -66,7 +66,7 @@ def lib():
         L.oracle_sigmoidf_array.argtypes = [i64, f32p, f32p]
         L.oracle_router_logits.argtypes = [i64, ctypes.c_int, ctypes.c_int, f32p, f32p, f32p, f32p]
         L.oracle_route.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_float, f32p, i32p, f32p, f32p, f32p, i32p]
+                                   ctypes.c_float, f32p, f32p, i32p, f32p, f32p, f32p, i32p]
         L.oracle_prenorm.argtypes = [i64, ctypes.c_int, f32p, f32p, ctypes.c_float, f32p, f32p]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -158,18 +158,23 @@ def router_logits(x32: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None
     return z
 
 
-def route(z: np.ndarray, G: int, Kg: int, K: int, alpha: float, details: bool = False):
-    """Group-limited top-K of sigmoid scores.  Returns ids [T,K] int32 (score
-    descending, ties to the lower index) and weights [T,K] FP32 (sum = alpha)."""
+def route(z: np.ndarray, G: int, Kg: int, K: int, alpha: float, details: bool = False,
+          select_bias: np.ndarray | None = None):
+    """Group-limited top-K of sigmoid scores.  Returns ids [T,K] int32 (ranking value
+    descending, ties to the lower index) and weights [T,K] FP32 (sum = alpha).  With a
+    select_bias [E], groups and experts are ranked by s + b (FP32) while the weights
+    normalise the unbiased scores s (auxiliary-loss-free balancing bias)."""
     z = np.ascontiguousarray(z, np.float32)
     T, E = z.shape
     assert E % G == 0 and E // G >= 2 and 1 <= Kg <= G and 1 <= K <= Kg * (E // G)
+    sb = None if select_bias is None else np.ascontiguousarray(select_bias, np.float32)
+    assert sb is None or sb.shape == (E,)
     ids = np.empty((T, K), np.int32)
     w = np.empty((T, K), np.float32)
     s = np.empty((T, E), np.float32) if details else None
     gs = np.empty((T, G), np.float32) if details else None
     gk = np.empty((T, Kg), np.int32) if details else None
-    lib().oracle_route(T, E, G, Kg, K, float(alpha), _f32p(z), _i32p(ids), _f32p(w),
+    lib().oracle_route(T, E, G, Kg, K, float(alpha), _f32p(z), _f32p(sb), _i32p(ids), _f32p(w),
                        _f32p(s), _f32p(gs), _i32p(gk))
     if details:
         return ids, w, {"scores": s, "group_scores": gs, "kept_groups": gk}
@@ -270,12 +275,12 @@ def residual_update(h64: np.ndarray, out64: np.ndarray, k: int) -> np.ndarray:
 # whole layer / sublayer
 # ---------------------------------------------------------------------------
 def moe_forward(x32: np.ndarray, w_router, bias, bank: ExpertBank, G, Kg, K, alpha,
-                token_subset: np.ndarray | None = None):
+                token_subset: np.ndarray | None = None, select_bias: np.ndarray | None = None):
     """One MoE layer on FP32 activations x32 [T,H].  Routing runs for every token;
     the expert MLPs and the combine run for `token_subset` (all tokens if None).
     Returns dict(ids, w, y [n,H] float64, tokens)."""
     z = router_logits(x32, w_router, bias)
-    ids, w = route(z, G, Kg, K, alpha)
+    ids, w = route(z, G, Kg, K, alpha, select_bias=select_bias)
     tok = np.arange(x32.shape[0]) if token_subset is None else np.asarray(token_subset)
     y = moe_combine(x32[tok].astype(np.float64), ids[tok], w[tok], bank)
     return {"ids": ids, "w": w, "y": y, "tokens": tok, "logits": z}
@@ -283,11 +288,11 @@ def moe_forward(x32: np.ndarray, w_router, bias, bank: ExpertBank, G, Kg, K, alp
 
 def sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, eps: float,
                      w_router, bias, bank: ExpertBank, G, Kg, K, alpha,
-                     token_subset: np.ndarray | None = None):
+                     token_subset: np.ndarray | None = None, select_bias: np.ndarray | None = None):
     """pre-RMSNorm (FP32, fixed order) -> MoE -> post-RMSNorm -> constant-scale residual.
     Returns dict(ids, w, y (MoE output), h_new (float64), tokens)."""
     xhat, _ = prenorm(h32, pre_gain, eps)
-    r = moe_forward(xhat, w_router, bias, bank, G, Kg, K, alpha, token_subset)
+    r = moe_forward(xhat, w_router, bias, bank, G, Kg, K, alpha, token_subset, select_bias)
     tok = r["tokens"]
     yn = rmsnorm64(r["y"], post_gain, eps)
     r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)

@@ -139,25 +139,37 @@ void oracle_router_logits(int64_t T, int H, int E, const float* x, const float* 
  * d = ((s_0 + s_1) + s_2) + ... summed in output order.
  * Optional outputs: s_out [T,E] scores, gscore_out [T,G] group scores,
  * gkept_out [T,Kg] kept groups in rank order.
+ *
+ * Optional selection bias sel_bias [E] (the auxiliary-loss-free balancing bias of the
+ * Beam training notes, section on pretraining foundations: "expert bias" updates keep
+ * expert load near uniform).  The pages do not say where it enters; the reading taken
+ * here: it is added to the scores for choosing only, r_e = s_e + b_e (one rounded FP32
+ * add), so groups are ranked by the top-2 sum of r and experts by r, while the weights
+ * still normalise the unbiased scores s of the picks.  NULL = no bias (r = s).
  */
 void oracle_route(int64_t T, int E, int G, int Kg, int K, float alpha, const float* z,
-                  int32_t* ids, float* w, float* s_out, float* gscore_out,
-                  int32_t* gkept_out)
+                  const float* sel_bias, int32_t* ids, float* w, float* s_out,
+                  float* gscore_out, int32_t* gkept_out)
 {
     const int S = E / G;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         float* s = (float*)malloc(sizeof(float) * (size_t)E);
+        float* rk = (float*)malloc(sizeof(float) * (size_t)E);
         float* gs = (float*)malloc(sizeof(float) * (size_t)G);
         char* kept = (char*)calloc((size_t)G, 1);
         char* taken = (char*)calloc((size_t)E, 1);
-        for (int e = 0; e < E; ++e) s[e] = oracle_sigmoidf(z[t * (int64_t)E + e]);
+        for (int e = 0; e < E; ++e) {
+            s[e] = oracle_sigmoidf(z[t * (int64_t)E + e]);
+            rk[e] = sel_bias ? s[e] + sel_bias[e] : s[e];
+        }
 
-        /* group score: top1 + top2 (as a multiset: a repeated maximum counts twice) */
+        /* group score: top1 + top2 of the ranking values (as a multiset: a repeated
+         * maximum counts twice) */
         for (int g = 0; g < G; ++g) {
-            float top1 = s[g * S], top2 = -INFINITY;
+            float top1 = rk[g * S], top2 = -INFINITY;
             for (int j = 1; j < S; ++j) {
-                const float v = s[g * S + j];
+                const float v = rk[g * S + j];
                 if (v > top1) { top2 = top1; top1 = v; }
                 else if (v > top2) top2 = v;
             }
@@ -176,7 +188,7 @@ void oracle_route(int64_t T, int E, int G, int Kg, int K, float alpha, const flo
         for (int i = 0; i < K; ++i) {
             int best = -1;
             for (int e = 0; e < E; ++e)
-                if (kept[e / S] && !taken[e] && (best < 0 || s[e] > s[best])) best = e;
+                if (kept[e / S] && !taken[e] && (best < 0 || rk[e] > rk[best])) best = e;
             taken[best] = 1;
             out[i] = best;
         }
@@ -189,7 +201,7 @@ void oracle_route(int64_t T, int E, int G, int Kg, int K, float alpha, const flo
             for (int e = 0; e < E; ++e) s_out[t * (int64_t)E + e] = s[e];
         if (gscore_out)
             for (int g = 0; g < G; ++g) gscore_out[t * (int64_t)G + g] = gs[g];
-        free(s); free(gs); free(kept); free(taken);
+        free(s); free(rk); free(gs); free(kept); free(taken);
     }
 }
 

@@ -176,6 +176,64 @@ def test_route_matches_brute_force_tiny_layer(seed):
         assert list(d["kept_groups"][t]) == exp_groups
 
 
+# Selection-only bias (auxiliary-loss-free balancing; reading: ranking value r = s + b in
+# FP32, weights from the unbiased scores s).
+@pytest.mark.parametrize("seed", range(4))
+def test_select_bias_matches_brute_force_tiny_layer(seed):
+    w = WORKLOADS["tiny_f32"]
+    rs = np.random.default_rng(100 + seed)
+    T = 48
+    z = rs.standard_normal((T, w.E)).astype(np.float32)
+    b = (rs.standard_normal(w.E) * 0.3).astype(np.float32)
+    if seed % 2:          # ties in the ranking values
+        b = np.round(b * 4) / 4
+        z = np.round(z * 2) / 2
+    ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True, select_bias=b)
+    s = d["scores"]
+    for t in range(T):
+        r = (s[t] + b).astype(np.float32)       # IEEE single-precision adds
+        exp_ids, exp_groups = brute_route(r, w.G, w.Kg, w.K)
+        assert list(ids[t]) == exp_ids, (t, ids[t], exp_ids)
+        assert list(d["kept_groups"][t]) == exp_groups
+        sel = s[t][ids[t]].astype(np.float64)
+        assert np.allclose(wts[t], w.alpha * sel / sel.sum(), rtol=1e-6, atol=0)
+
+
+def test_select_bias_zero_is_the_unbiased_route():
+    w = WORKLOADS["beam_decode_t16"]
+    z = np.random.default_rng(7).standard_normal((64, w.E)).astype(np.float32)
+    i0, w0 = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    i1, w1 = oracle.route(z, w.G, w.Kg, w.K, w.alpha, select_bias=np.zeros(w.E, np.float32))
+    assert np.array_equal(i0, i1) and np.array_equal(w0, w1)
+
+
+def test_select_bias_dominant_bias_forces_the_picks():
+    """A bias of +8 on two experts in each of Kg chosen groups (scores lie in (0, 1))
+    forces exactly those K experts whatever the logits; -8 on the natural winner
+    removes it.  Weights normalise the unbiased scores of the forced picks."""
+    w = WORKLOADS["beam_decode_t16"]
+    S = w.E // w.G
+    rs = np.random.default_rng(11)
+    z = rs.standard_normal((32, w.E)).astype(np.float32)
+    forced = np.array([g * S + j for g in (1, 3, 4, 6) for j in (5, 17)])
+    b = np.zeros(w.E, np.float32)
+    b[forced] = 8.0
+    ids, wts, d = oracle.route(z, w.G, w.Kg, w.K, w.alpha, details=True, select_bias=b)
+    s = d["scores"]
+    for t in range(z.shape[0]):
+        r = (s[t][forced] + np.float32(8.0)).astype(np.float32)
+        order = sorted(range(len(forced)), key=lambda i: (-float(r[i]), int(forced[i])))
+        assert list(ids[t]) == [int(forced[i]) for i in order]
+        assert sorted(d["kept_groups"][t]) == [1, 3, 4, 6]
+        sel = s[t][ids[t]].astype(np.float64)
+        assert np.allclose(wts[t], w.alpha * sel / sel.sum(), rtol=1e-6, atol=0)
+    top, _ = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    b2 = np.zeros(w.E, np.float32)
+    b2[top[0, 0]] = -8.0
+    ids2, _ = oracle.route(z[:1], w.G, w.Kg, w.K, w.alpha, select_bias=b2)
+    assert top[0, 0] not in ids2[0]
+
+
 def dominance_ok(s, gs, kept, ids, G, K):
     E = s.size
     S = E // G
