@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BEAM_MOE_ABI_VERSION 1
+#define BEAM_MOE_ABI_VERSION 2
 
 typedef enum {
     BEAM_OK = 0,
@@ -108,25 +108,33 @@ size_t beam_moe_workspace_size(const beam_moe_config* cfg, int64_t T);
  *   x          device [T, H], act_dtype (BF16 values are widened exactly to FP32)
  *   w_router   device [H, E] FP32
  *   logit_bias device [E] FP32 added to each logit before the sigmoid, or NULL
- *   ids        device [T, K] int32 out: expert ids, score-descending, ties -> lower id
+ *   select_bias device [E] FP32 or NULL: a choosing-only expert bias (the balancing
+ *              "expert bias" of the Beam training notes, pretraining foundations; the
+ *              pages do not say where it enters -- read here as: groups and experts
+ *              are ranked by r = s + b, one rounded FP32 add, while the weights
+ *              normalise the unbiased scores s of the picks).  NULL: r = s.
+ *   ids        device [T, K] int32 out: expert ids, ranking-value-descending, ties ->
+ *              lower id
  *   weights    device [T, K] FP32 out: combine weights, summing to alpha per token
  *   ws         device workspace of ws_bytes >= beam_moe_workspace_size(cfg, T)
  */
 int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
-                   const float* w_router, const float* logit_bias, int32_t* ids,
-                   float* weights, void* ws, size_t ws_bytes, void* stream);
+                   const float* w_router, const float* logit_bias,
+                   const float* select_bias, int32_t* ids, float* weights, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /*
  * One MoE layer (Beam overview, "Mixture of Experts"):
  *   y[t] = sum_{i<K} w[t,i] * Wd_e (SiLU(Wg_e x_t) * (Wu_e x_t)),  e = ids[t,i].
  *   x          device [T, H] act_dtype
- *   w_router   device [H, E] FP32;  logit_bias device [E] FP32 or NULL
+ *   w_router   device [H, E] FP32;  logit_bias, select_bias device [E] FP32 or NULL
+ *              (as in beam_moe_route)
  *   w13        device [E, 2I, H] weight_dtype: rows 0..I-1 gate, rows I..2I-1 up,
  *              each row H-contiguous
  *   w13_scale  FP8 only: device [E, 2I/128, H/128] FP32 block scales (value =
  *              code * scale of its 128x128 tile); must be NULL otherwise.  Each
  *              scale must be a normal power of two (an E8M0 block exponent): above
- *              32 tokens the matrix cores apply only its exponent field.
+ *              256 tokens the matrix cores apply only its exponent field.
  *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous)
  *   w2_scale   FP8 only: device [E, H/128, I/128] FP32 powers of two; NULL otherwise
  *   y          device [T, H] act_dtype out
@@ -135,7 +143,8 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  * with one FP32 scale per row (the row's amax / 448).
  */
 int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x,
-                     const float* w_router, const float* logit_bias, const void* w13,
+                     const float* w_router, const float* logit_bias,
+                     const float* select_bias, const void* w13,
                      const float* w13_scale, const void* w2, const float* w2_scale,
                      void* y, int32_t* ids_out, float* weights_out, void* ws,
                      size_t ws_bytes, void* stream);
@@ -158,7 +167,8 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x,
 int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
                               const float* pre_gain, const float* post_gain,
                               int32_t step_k, const float* w_router,
-                              const float* logit_bias, const void* w13,
+                              const float* logit_bias, const float* select_bias,
+                              const void* w13,
                               const float* w13_scale, const void* w2,
                               const float* w2_scale, void* moe_out, int32_t* ids_out,
                               float* weights_out, void* ws, size_t ws_bytes, void* stream);

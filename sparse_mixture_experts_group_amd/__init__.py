@@ -74,12 +74,12 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_workspace_map.restype = ctypes.c_int
     L.beam_moe_workspace_map.argtypes = [cfgp, i64, ctypes.POINTER(beam_moe_ws_map)]
     L.beam_moe_route.restype = ctypes.c_int
-    L.beam_moe_route.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_route.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_forward.restype = ctypes.c_int
-    L.beam_moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_sublayer_forward.restype = ctypes.c_int
     L.beam_moe_sublayer_forward.argtypes = [cfgp, i64, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, vp, sz, vp]
+                                            vp, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_time_kernel.restype = ctypes.c_int
     L.beam_moe_time_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     _lib = L
@@ -139,7 +139,8 @@ def alloc_workspace(cfg: beam_moe_config, T: int, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def beam_moe_route(cfg, x, w_router, logit_bias=None, ids=None, weights=None, ws=None, stream=None):
+def beam_moe_route(cfg, x, w_router, logit_bias=None, ids=None, weights=None, ws=None, stream=None,
+                   select_bias=None):
     """Router: returns (ids [T,K] int32, weights [T,K] float32) on the GPU."""
     import torch
     T = x.shape[0]
@@ -147,21 +148,21 @@ def beam_moe_route(cfg, x, w_router, logit_bias=None, ids=None, weights=None, ws
     ids = torch.empty((T, K), dtype=torch.int32, device=x.device) if ids is None else ids
     weights = torch.empty((T, K), dtype=torch.float32, device=x.device) if weights is None else weights
     ws = alloc_workspace(cfg, T, x.device) if ws is None else ws
-    st = lib().beam_moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(ids),
-                              _ptr(weights), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    st = lib().beam_moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+                              _ptr(ids), _ptr(weights), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "beam_moe_route")
     return ids, weights
 
 
 def beam_moe_forward(cfg, x, w_router, w13, w2, logit_bias=None, w13_scale=None, w2_scale=None, y=None,
-                     ids=None, weights=None, ws=None, stream=None):
+                     ids=None, weights=None, ws=None, stream=None, select_bias=None):
     """One MoE layer: returns y [T,H] (same dtype as x) on the GPU."""
     import torch
     T = x.shape[0]
     y = torch.empty_like(x) if y is None else y
     ws = alloc_workspace(cfg, T, x.device) if ws is None else ws
-    st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w13),
-                                _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(ids), _ptr(weights),
+    st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                _ptr(select_bias), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(ids), _ptr(weights),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "beam_moe_forward")
     return y
@@ -195,12 +196,13 @@ class KernelTimer:
 
 def beam_moe_sublayer_forward(cfg, h, step_k, w_router, w13, w2, pre_gain=None, post_gain=None,
                               logit_bias=None, w13_scale=None, w2_scale=None, moe_out=None, ids=None,
-                              weights=None, ws=None, stream=None):
+                              weights=None, ws=None, stream=None, select_bias=None):
     """pre-RMSNorm -> MoE -> post-RMSNorm -> constant-scale residual, updating h in place."""
     T = h.shape[0]
     ws = alloc_workspace(cfg, T, h.device) if ws is None else ws
     st = lib().beam_moe_sublayer_forward(ctypes.byref(cfg), T, _ptr(h), _ptr(pre_gain), _ptr(post_gain),
-                                         int(step_k), _ptr(w_router), _ptr(logit_bias), _ptr(w13),
+                                         int(step_k), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+                                         _ptr(w13),
                                          _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(moe_out), _ptr(ids),
                                          _ptr(weights), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(stream))

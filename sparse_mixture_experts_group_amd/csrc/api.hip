@@ -156,7 +156,7 @@ int launch_status() {
 // Router + permutation.  x_router is FP32 or BF16 [T, H].
 void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
                 const void* x_router, bool x_bf16, const float* w_router, const float* bias,
-                int32_t* ids, float* wts, bool permute) {
+                const float* select_bias, int32_t* ids, float* wts, bool permute) {
     const int E = c.n_experts, K = c.topk;
     float* z = at<float>(ws, L.z);
     {
@@ -164,8 +164,8 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
         launch_router_logits(st, static_cast<int>(T), c.hidden, E, x_bf16, x_router, w_router, bias, z,
                              at<float>(ws, L.zpart));
     }
-    launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, ids, wts,
-                         at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
+    launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, select_bias,
+                         ids, wts, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
     if (!permute) return;
     if (L.nblk <= kFinishSmallBlocks) {
         launch_route_finish_small(st, static_cast<int>(T), K, E, L.nblk, L.bm, ids, at<int32_t>(ws, L.pair_rank),
@@ -287,8 +287,8 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
 }
 
 int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
-                   const float* logit_bias, int32_t* ids, float* weights, void* ws, size_t ws_bytes,
-                   void* stream) {
+                   const float* logit_bias, const float* select_bias, int32_t* ids, float* weights, void* ws,
+                   size_t ws_bytes, void* stream) {
     int s = check_common(cfg, T);
     if (s != BEAM_OK) return s;
     if (cfg->act_dtype == BEAM_DTYPE_FP8_E4M3) return BEAM_ERR_UNSUPPORTED;
@@ -299,7 +299,8 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const f
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
     clear_hip_error();
-    run_router(*cfg, T, L, ws, st, x, cfg->act_dtype == BEAM_DTYPE_BF16, w_router, logit_bias, ids, weights, false);
+    run_router(*cfg, T, L, ws, st, x, cfg->act_dtype == BEAM_DTYPE_BF16, w_router, logit_bias, select_bias, ids,
+               weights, false);
     return launch_status();
 }
 
@@ -313,7 +314,8 @@ static int check_weights(const beam_moe_config* cfg, const void* w13, const floa
 }
 
 int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
-                     const float* logit_bias, const void* w13, const float* w13_scale, const void* w2,
+                     const float* logit_bias, const float* select_bias, const void* w13,
+                     const float* w13_scale, const void* w2,
                      const float* w2_scale, void* y, int32_t* ids_out, float* weights_out, void* ws,
                      size_t ws_bytes, void* stream) {
     int s = check_common(cfg, T);
@@ -329,7 +331,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
     int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
     float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
     const bool bf16_act = cfg->act_dtype == BEAM_DTYPE_BF16;
-    run_router(*cfg, T, L, ws, st, x, bf16_act, w_router, logit_bias, ids, wts, true);
+    run_router(*cfg, T, L, ws, st, x, bf16_act, w_router, logit_bias, select_bias, ids, wts, true);
     const void* x_exp = x;
     const float* x_exp_scale = nullptr;
     if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3) {
@@ -346,7 +348,8 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
 
 int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, const float* pre_gain,
                               const float* post_gain, int32_t step_k, const float* w_router,
-                              const float* logit_bias, const void* w13, const float* w13_scale,
+                              const float* logit_bias, const float* select_bias, const void* w13,
+                              const float* w13_scale,
                               const void* w2, const float* w2_scale, void* moe_out, int32_t* ids_out,
                               float* weights_out, void* ws, size_t ws_bytes, void* stream) {
     int s = check_common(cfg, T);
@@ -368,7 +371,8 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, co
     launch_prenorm(st, T, H, static_cast<const uint16_t*>(h), pre_gain, cfg->norm_eps, at<float>(ws, L.xhat32),
                    fp8 ? nullptr : at<uint16_t>(ws, L.x16), fp8 ? at<uint8_t>(ws, L.x8) : nullptr,
                    fp8 ? at<float>(ws, L.x8s) : nullptr);
-    run_router(*cfg, T, L, ws, st, at<float>(ws, L.xhat32), false, w_router, logit_bias, ids, wts, true);
+    run_router(*cfg, T, L, ws, st, at<float>(ws, L.xhat32), false, w_router, logit_bias, select_bias, ids, wts,
+               true);
     const void* x_exp = fp8 ? at<void>(ws, L.x8) : at<void>(ws, L.x16);
     const float* x_exp_scale = fp8 ? at<float>(ws, L.x8s) : nullptr;
     run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids);

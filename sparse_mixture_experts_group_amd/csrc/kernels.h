@@ -45,7 +45,8 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, const void* x,
                           const float* wr, const float* bias, float* z, float* part);
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
-                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt, int32_t* pair_rank);
+                          const float* z, const float* sel_bias, int32_t* ids, float* wts, int32_t* blk_cnt,
+                          int32_t* pair_rank);
 void launch_route_scan(hipStream_t st, int nblk, int E, int BM, const int32_t* blk_cnt,
                        int32_t* blk_off, int32_t* exp_cnt, int32_t* exp_off, int2* tiles,
                        int32_t* meta, int32_t* active);

@@ -234,9 +234,14 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int T, int H, int E, 
 // its first maximum).  The block also records, for the stable token -> expert
 // permutation, how many of its pairs go to each expert and each pair's rank among the
 // block's pairs with the same expert.
+// Optional selection bias (the balancing "expert bias" of the Beam training notes,
+// pretraining foundations section; how it enters routing is not on the pages -- read
+// here as a choosing-only bias): groups and experts are ranked by s + b, the weights
+// normalise the unbiased scores s of the picks.
 template <int V>
 __global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E, int G, int Kg, int K,
                                                      float alpha, const float* __restrict__ z,
+                                                     const float* __restrict__ sel_bias,
                                                      int32_t* __restrict__ ids,
                                                      float* __restrict__ wts,
                                                      int32_t* __restrict__ blk_cnt,
@@ -256,19 +261,22 @@ __global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E
         const int tl = wave;
         const int t = t0 + tl;
         if (t >= T) goto done;
-        float s[V];
+        // s: scores (they weight the picks); rk: ranking values, s + b with a selection
+        // bias (one rounded add), else s
+        float s[V], rk[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int e = lane * V + v;
-            s[v] = (e < E) ? router_sigmoid(z[static_cast<int64_t>(t) * E + e]) : -1.0f;
+            s[v] = (e < E) ? router_sigmoid(z[static_cast<int64_t>(t) * E + e]) : -INFINITY;
+            rk[v] = (e < E && sel_bias) ? __fadd_rn(s[v], sel_bias[e]) : s[v];
         }
-        // group top-2 (multiset: a repeated maximum counts twice)
+        // group top-2 of the ranking values (multiset: a repeated maximum counts twice)
         float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             if (lane * V + v >= E) continue;
-            if (s[v] > a1) { a2 = a1; a1 = s[v]; }
-            else if (s[v] > a2) a2 = s[v];
+            if (rk[v] > a1) { a2 = a1; a1 = rk[v]; }
+            else if (rk[v] > a2) a2 = rk[v];
         }
         for (int o = 1; o < L; o <<= 1) {
             const float b1 = __shfl_xor(a1, o, kWave), b2 = __shfl_xor(a2, o, kWave);
@@ -287,29 +295,31 @@ __global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E
             kept |= 1ull << ((wl * V) / S);
             if (lane == wl) gv = -INFINITY;
         }
-        // candidates: experts inside kept groups only
+        // candidates: experts inside kept groups only (-inf marks the others and the
+        // picks already taken; ranking values may be negative with a bias)
         const bool gk = lane_live && ((kept >> group) & 1ull);
         float c[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) c[v] = (gk && lane * V + v < E) ? s[v] : -1.0f;
+        for (int v = 0; v < V; ++v) c[v] = (gk && lane * V + v < E) ? rk[v] : -INFINITY;
 
         int my_id = 0;
         float my_s = 0.0f;
         for (int i = 0; i < K; ++i) {
-            float lb = c[0];
+            float lb = c[0], ls = s[0];
             int lv = 0;
 #pragma unroll
             for (int v = 1; v < V; ++v)
-                if (c[v] > lb) { lb = c[v]; lv = v; }
+                if (c[v] > lb) { lb = c[v]; ls = s[v]; lv = v; }
             const float m = wave_max(lb);
             const int wl = first_lane(wave_ballot(lb == m));
             const int wv = __shfl(lv, wl, kWave);
+            const float ps = __shfl(ls, wl, kWave);      // the pick's unbiased score
             if (lane == wl) {
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    if (v == lv) c[v] = -1.0f;
+                    if (v == lv) c[v] = -INFINITY;
             }
-            if (lane == i) { my_id = wl * V + wv; my_s = m; }
+            if (lane == i) { my_id = wl * V + wv; my_s = ps; }
         }
         float d = 0.0f;
         for (int i = 0; i < K; ++i) d = __fadd_rn(d, __shfl(my_s, i, kWave));
@@ -504,11 +514,12 @@ void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, cons
 }
 
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
-                          const float* z, int32_t* ids, float* wts, int32_t* blk_cnt, int32_t* pair_rank) {
+                          const float* z, const float* sel_bias, int32_t* ids, float* wts, int32_t* blk_cnt,
+                          int32_t* pair_rank) {
     const int nblk = (T + kSelectTokens - 1) / kSelectTokens;
     const int V = scores_per_lane(E);
     const int nt = kSelectTokens * 64;
-#define BEAM_SEL(VV) router_select<VV><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, ids, wts, blk_cnt, pair_rank)
+#define BEAM_SEL(VV) router_select<VV><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, sel_bias, ids, wts, blk_cnt, pair_rank)
     if (V == 1) BEAM_SEL(1);
     else if (V == 2) BEAM_SEL(2);
     else BEAM_SEL(4);

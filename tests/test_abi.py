@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = bm.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert bm.abi_version() == 1
+    assert bm.abi_version() == 2
 
 
 def test_status_strings():
@@ -60,8 +60,8 @@ def test_workspace_size_and_map():
                                 dict(act_dtype=7)])
 def test_invalid_config_rejected(kw):
     c = beam(**kw)
-    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
-                                   None, FAKE, 1 << 40, None)
+    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, None, FAKE, None, FAKE, None, FAKE,
+                                   None, None, FAKE, 1 << 40, None)
     assert st == bm.BEAM_ERR_INVALID_ARG
 
 
@@ -70,8 +70,8 @@ def test_invalid_config_rejected(kw):
                                 dict(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3, fp8_block=64)])
 def test_unsupported_config(kw):
     c = beam(**kw)
-    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
-                                   None, FAKE, 1 << 40, None)
+    st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, None, FAKE, None, FAKE, None, FAKE,
+                                   None, None, FAKE, 1 << 40, None)
     assert st == bm.BEAM_ERR_UNSUPPORTED
 
 
@@ -79,7 +79,7 @@ def test_argument_errors_before_any_launch():
     c = beam()
     L = bm.lib()
     fwd = lambda T, x, y, ws, nb, w13=FAKE, s13=None: L.beam_moe_forward(
-        ctypes.byref(c), T, x, FAKE, None, w13, s13, FAKE, None, y, None, None, ws, nb, None)
+        ctypes.byref(c), T, x, FAKE, None, None, w13, s13, FAKE, None, y, None, None, ws, nb, None)
     assert fwd(0, None, None, None, 0) == bm.BEAM_OK                   # T = 0: no-op
     assert fwd(-1, FAKE, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
     assert fwd(16, None, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
@@ -92,20 +92,21 @@ def test_argument_errors_before_any_launch():
     assert fwd(16, FAKE, FAKE, None, need) == bm.BEAM_ERR_WORKSPACE
     # FP8 weights need both scale arrays
     c8 = beam(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3)
-    st = L.beam_moe_forward(ctypes.byref(c8), 16, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None, None,
-                            FAKE, 1 << 40, None)
+    st = L.beam_moe_forward(ctypes.byref(c8), 16, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, None,
+                            None, FAKE, 1 << 40, None)
     assert st == bm.BEAM_ERR_INVALID_ARG
 
 
 def test_route_and_sublayer_argument_errors():
     c = beam()
     L = bm.lib()
-    assert L.beam_moe_route(ctypes.byref(c), 16, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 40,
+    assert L.beam_moe_route(ctypes.byref(c), 16, FAKE, FAKE, None, None, None, FAKE, FAKE, 1 << 40,
                             None) == bm.BEAM_ERR_INVALID_ARG
-    assert L.beam_moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, 0, None) == bm.BEAM_OK
+    assert L.beam_moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, None, 0,
+                            None) == bm.BEAM_OK
     sub = lambda cfg, k, ws_bytes: L.beam_moe_sublayer_forward(
-        ctypes.byref(cfg), 16, FAKE, None, None, k, FAKE, None, FAKE, None, FAKE, None, None, None, None, FAKE,
-        ws_bytes, None)
+        ctypes.byref(cfg), 16, FAKE, None, None, k, FAKE, None, None, FAKE, None, FAKE, None, None, None, None,
+        FAKE, ws_bytes, None)
     assert sub(c, 1, 1 << 40) == bm.BEAM_ERR_INVALID_ARG                 # step k must be >= 2
     assert sub(beam(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_F32), 10,
                1 << 40) == bm.BEAM_ERR_UNSUPPORTED

@@ -53,7 +53,7 @@ def sample_tokens(T, n=16, seed=1):
     return np.array(sorted(base | set(int(t) for t in extra)))[:max(n, 3)]
 
 
-def run_forward(w, dev, x, bias):
+def run_forward(w, dev, x, bias, select_bias=None):
     cfg = cfg_of(w)
     xd = to_dev_x(w, x)
     ids = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
@@ -61,7 +61,7 @@ def run_forward(w, dev, x, bias):
     ws = bm.alloc_workspace(cfg, w.T)
     y = bm.beam_moe_forward(cfg, xd, dev["w_router"], dev["w13"], dev["w2"], logit_bias=dev_bias(bias),
                             w13_scale=dev.get("w13_scale"), w2_scale=dev.get("w2_scale"), ids=ids, weights=wts,
-                            ws=ws)
+                            ws=ws, select_bias=dev_bias(select_bias))
     torch.cuda.synchronize()
     return cfg, y, ids.cpu().numpy(), wts.cpu().numpy(), ws
 
@@ -118,6 +118,47 @@ def test_tiny_layer_ragged_T(T):
     check_routing(w, ids, wts, ref["ids"], ref["w"])
     check_permutation(w, ws, ids)
     assert rel_inf(y.cpu().numpy().astype(np.float64), ref["y"]) <= TOL[DT_F32]
+
+
+# ---------------------------------------------------------------------------
+# selection-only expert bias (ranking on s + b, weights from s)
+# ---------------------------------------------------------------------------
+def test_select_bias_tiny_layer_full_parity():
+    w, full, dev, x, bias = gpu_inputs("tiny_f32")
+    sb = (np.random.default_rng(21).standard_normal(w.E) * 0.2).astype(np.float32)
+    print(f"[case] tiny_f32 select bias T={w.T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, bias, select_bias=sb)
+    ref = oracle.moe_forward(x_f32(w, x), full.w_router, bias, bank_of(w, full), w.G, w.Kg, w.K, w.alpha,
+                             select_bias=sb)
+    check_routing(w, ids, wts, ref["ids"], ref["w"])
+    check_permutation(w, ws, ids)
+    assert rel_inf(y.cpu().numpy().astype(np.float64), ref["y"]) <= TOL[DT_F32]
+    ref0 = oracle.moe_forward(x_f32(w, x), full.w_router, bias, bank_of(w, full), w.G, w.Kg, w.K, w.alpha)
+    assert not np.array_equal(ref0["ids"], ref["ids"])      # the bias does change the routing
+
+
+@pytest.mark.parametrize("T", [16, 300, 4096])
+def test_select_bias_beam_routing(T):
+    """Beam-shaped routing with a random selection bias (chunk-parallel and tiled logits
+    kernels) and with a dominant bias forcing two experts in each of four groups."""
+    w, full, dev, x, bias = gpu_inputs("beam_prefill_t4096", T)
+    cfg = cfg_of(w)
+    xd = to_dev_x(w, x)
+    x32 = x_f32(w, x)
+    z = oracle.router_logits(x32, full.w_router, bias)
+    S = w.E // w.G
+    forced = np.array([g * S + j for g in (0, 2, 5, 7) for j in (3, 30)])
+    dominant = np.zeros(w.E, np.float32)
+    dominant[forced] = 8.0
+    for name, sb in (("random", (np.random.default_rng(22).standard_normal(w.E) * 0.02).astype(np.float32)),
+                     ("dominant", dominant)):
+        print(f"[case] beam routing T={T} select bias {name}", flush=True)
+        ids, wts = bm.beam_moe_route(cfg, xd, dev["w_router"], logit_bias=dev_bias(bias), select_bias=dev_bias(sb))
+        torch.cuda.synchronize()
+        rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha, select_bias=sb)
+        check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+        if name == "dominant":
+            assert np.array_equal(np.sort(rid, axis=1), np.tile(np.sort(forced), (T, 1)))
 
 
 def test_router_all_ties_and_duplicated_columns():
