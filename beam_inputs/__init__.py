@@ -33,8 +33,8 @@ TAG_W2 = 4
 TAG_PERM = 5
 TAG_H = 6
 
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
-DTYPE_NAMES = {DT_F32: "f32", DT_BF16: "bf16", DT_FP8: "fp8_e4m3"}
+DT_F32, DT_BF16, DT_FP8, DT_MXFP4 = 0, 1, 2, 3
+DTYPE_NAMES = {DT_F32: "f32", DT_BF16: "bf16", DT_FP8: "fp8_e4m3", DT_MXFP4: "mxfp4"}
 
 
 def _threads() -> int:
@@ -121,6 +121,54 @@ def quantize_e4m3_blocks(w: np.ndarray, block: int = 128):
     return codes, scale
 
 
+# MXFP4 (OCP Microscaling Formats (MX) v1.0): blocks of 32 consecutive values along K
+# share one E8M0 scale 2^X; the elements are FP4 E2M1 (sign, 2 exponent bits with bias
+# 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+E2M1_EMAX = 2          # exponent of the largest normal E2M1 value (6 = 1.5 * 2^2)
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """Encode values (already divided by their block scale) as E2M1 codes (uint8, low 4
+    bits): round to nearest, ties to the even code (mantissa bit 0), saturating at +-6."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    # steps: 0.5 below 2, 1 in [2, 4), 2 in [4, 6]
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    q = np.rint(a / step) * step                       # rint: ties to even multiples
+    q = np.minimum(q, E2M1_MAX)
+    # q is on the grid; code: 0..1 subnormal/zero (0, 0.5), then (e, m)
+    _, e = np.frexp(np.where(q > 0, q, 1.0))
+    e = e - 1                                          # q = 1.m * 2^e for q >= 1
+    exp_field = np.where(q >= 1.0, e + 1, 0)
+    mant = np.where(q >= 1.0, q / np.ldexp(1.0, e) - 1.0, q / 0.5) * 2.0
+    mant = np.where(q >= 1.0, mant, q / 0.5)
+    code = (exp_field.astype(np.int64) << 1) | np.rint(mant).astype(np.int64)
+    code = np.where(q == 0, 0, code)
+    code |= np.where(np.signbit(v) & (q > 0), 0x8, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """MX quantisation of a [N, K] float32 matrix along K.
+
+    Per block of 32: X = floor(log2(amax)) - 2 (the E2M1 emax), scale 2^X stored as the
+    E8M0 code X + 127 (an all-zero block gets code 127), elements E2M1(w / 2^X) with
+    round-to-nearest-even and saturation at +-6.  Returns (packed codes uint8 [N, K/2],
+    element 2j in the low nibble of byte j; scales uint8 [N, K/32])."""
+    n, k = w.shape
+    assert k % MX_BLOCK == 0
+    t = w.reshape(n, k // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.abs(t).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, (ex - 1) - E2M1_EMAX, 0)
+    X = np.clip(X, -127, 127)
+    codes = encode_e2m1(t / np.ldexp(1.0, X)[:, :, None]).reshape(n, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
@@ -165,6 +213,9 @@ WORKLOADS = {
     # full sublayer with FP8 experts
     "beam_sublayer_fp8_t8192": Workload("beam_sublayer_fp8_t8192", T=8192, H=5120, I=2560, E=256, G=8,
                                         Kg=4, K=8, weight_dtype=DT_FP8, sublayer=True),
+    # decode batch with MXFP4 experts (E2M1 elements, E8M0 scale per 32 along K)
+    "beam_decode_mxfp4_t16": Workload("beam_decode_mxfp4_t16", T=16, H=5120, I=2560, E=256, G=8, Kg=4, K=8,
+                                      weight_dtype=DT_MXFP4, x_recipe="rms_normal"),
 }
 
 
@@ -243,14 +294,20 @@ def make_inputs(w: Workload, experts: list[int] | None = None) -> Inputs:
     elif w.weight_dtype == DT_BF16:
         w13 = np.zeros((E, 2 * I, H), np.uint16)
         w2 = np.zeros((E, H, I), np.uint16)
-    else:
+    elif w.weight_dtype == DT_FP8:
         w13 = np.zeros((E, 2 * I, H), np.uint8)
         w2 = np.zeros((E, H, I), np.uint8)
+    else:
+        w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+        w2 = np.zeros((E, H, I // 2), np.uint8)
     s13 = s2 = None
     if w.weight_dtype == DT_FP8:
         b = w.fp8_block
         s13 = np.ones((E, 2 * I // b, H // b), np.float32)
         s2 = np.ones((E, H // b, I // b), np.float32)
+    elif w.weight_dtype == DT_MXFP4:
+        s13 = np.full((E, 2 * I, H // MX_BLOCK), 127, np.uint8)
+        s2 = np.full((E, H, I // MX_BLOCK), 127, np.uint8)
 
     todo = list(range(E)) if experts is None else sorted(set(experts))
 
@@ -260,9 +317,12 @@ def make_inputs(w: Workload, experts: list[int] | None = None) -> Inputs:
             w13[e], w2[e] = g13, g2
         elif w.weight_dtype == DT_BF16:
             w13[e], w2[e] = to_bf16_bits(g13), to_bf16_bits(g2)
-        else:
+        elif w.weight_dtype == DT_FP8:
             w13[e], s13[e] = quantize_e4m3_blocks(g13, w.fp8_block)
             w2[e], s2[e] = quantize_e4m3_blocks(g2, w.fp8_block)
+        else:
+            w13[e], s13[e] = quantize_mxfp4(g13)
+            w2[e], s2[e] = quantize_mxfp4(g2)
 
     if len(todo) > 1:
         with ThreadPoolExecutor(_threads()) as ex:

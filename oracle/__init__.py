@@ -127,6 +127,41 @@ def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndar
             * scales.astype(np.float64)[:, None, :, None]).reshape(n, k)
 
 
+def _e2m1_table() -> np.ndarray:
+    """Value of each of the 16 FP4 E2M1 codes (OCP Microscaling Formats v1.0, element
+    format FP4): sign bit, 2-bit exponent (bias 1), 1-bit mantissa; exponent field 0
+    encodes the subnormal m/2 * 2^0; no infinity or NaN."""
+    tab = np.empty(16, np.float64)
+    for c in range(16):
+        sign = -1.0 if c & 0x8 else 1.0
+        ex = (c >> 1) & 0x3
+        m = c & 0x1
+        tab[c] = sign * ((m / 2.0) if ex == 0 else (1.0 + m / 2.0) * 2.0 ** (ex - 1))
+    return tab
+
+
+E2M1_TABLE = _e2m1_table()
+
+
+def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale (OCP MX v1.0): 2^(code - 127); code 255 is NaN."""
+    c = np.asarray(codes, np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """Stored value of an MXFP4 matrix [N, K]: packed [N, K/2] bytes (element 2j in the
+    low nibble of byte j, 2j+1 in the high nibble), scales [N, K/block] E8M0; value =
+    E2M1 element * its block's scale (exact in float64)."""
+    p = np.asarray(packed, np.uint8)
+    n, kh = p.shape
+    codes = np.empty((n, 2 * kh), np.uint8)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    v = E2M1_TABLE[codes]
+    return (v.reshape(n, -1, block) * e8m0_to_f64(scales)[:, :, None]).reshape(n, 2 * kh)
+
+
 # ---------------------------------------------------------------------------
 # FP32 router (C)
 # ---------------------------------------------------------------------------
@@ -226,6 +261,8 @@ class ExpertBank:
         if self.dtype == "fp8_e4m3":
             return (dequant_blocks(self.w13[e], self.s13[e], self.block),
                     dequant_blocks(self.w2[e], self.s2[e], self.block))
+        if self.dtype == "mxfp4":
+            return dequant_mxfp4(self.w13[e], self.s13[e]), dequant_mxfp4(self.w2[e], self.s2[e])
         raise ValueError(self.dtype)
 
 

@@ -3,7 +3,8 @@ import numpy as np
 import torch
 
 import oracle
-from beam_inputs import (WORKLOADS, encode_e4m3, make_inputs, quantize_e4m3_blocks, to_bf16_bits,
+from beam_inputs import (WORKLOADS, encode_e4m3, encode_e2m1, make_inputs, quantize_e4m3_blocks, quantize_mxfp4,
+                         to_bf16_bits,
                          token_inputs, zipf_logit_offsets, normal)
 
 
@@ -47,6 +48,45 @@ def test_block_quantisation_power_of_two_scales():
     assert np.all(deq[128:, 256:] == 0.0)
     rel = np.abs(deq - w) / np.abs(w).max()
     assert rel.max() <= 2.0 ** -4 + 1e-6      # half a step of a 3-bit mantissa at amax
+
+
+def test_e2m1_encoder_round_to_nearest_even_and_saturation():
+    grid = oracle.E2M1_TABLE[:8]
+    # every representable value round-trips; midpoints go to the even code
+    assert np.array_equal(oracle.E2M1_TABLE[encode_e2m1(grid)], grid)
+    assert np.array_equal(oracle.E2M1_TABLE[encode_e2m1(-grid[1:])], -grid[1:])
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    assert np.array_equal(oracle.E2M1_TABLE[encode_e2m1(mids)], [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+    assert np.array_equal(oracle.E2M1_TABLE[encode_e2m1(np.array([6.5, 100.0, -7.0]))], [6.0, 6.0, -6.0])
+    # off-midpoint values go to the nearest grid point
+    v = np.random.default_rng(3).uniform(-6, 6, 20000)
+    got = oracle.E2M1_TABLE[encode_e2m1(v)]
+    dist = np.abs(v[:, None] - np.concatenate([grid, -grid])[None, :]).min(axis=1)
+    assert np.allclose(np.abs(got - v), dist)
+
+
+def test_mxfp4_block_scales_follow_the_mx_rule():
+    """X = floor(log2(amax)) - 2 per block of 32 along K (OCP MX v1.0 conversion with the
+    E2M1 emax of 2); amax / 2^X lies in [4, 8), so the block maximum rounds to 4 or 6."""
+    w = normal(0, (9,), (64, 256), std=0.02)
+    w[3, 32:64] = 0.0
+    packed, sc = quantize_mxfp4(w)
+    assert packed.shape == (64, 128) and sc.shape == (64, 8)
+    amax = np.abs(w.reshape(64, 8, 32)).max(axis=2).astype(np.float64)
+    X = sc.astype(np.int64) - 127
+    nz = amax > 0
+    assert np.array_equal(X[nz], np.floor(np.log2(amax[nz])).astype(np.int64) - 2)
+    assert sc[3, 1] == 127
+    deq = oracle.dequant_mxfp4(packed, sc)
+    assert np.all(deq[3, 32:64] == 0.0)
+    # elements up to 6 * 2^X lie within half a grid step (at most 2^X at the top, where
+    # the step is 2 * 2^X); larger ones saturate to 6 * 2^X (amax / 2^X < 8)
+    scale = np.repeat(np.ldexp(1.0, X), 32, axis=1)
+    err = np.abs(deq - w)
+    inside = np.abs(w) <= 6.0 * scale
+    assert np.all(err[inside] <= scale[inside] + 1e-12)
+    assert np.all(deq[~inside] == np.sign(w[~inside]) * 6.0 * scale[~inside])
+    assert np.all(err < 2.0 * scale)
 
 
 def test_prefix_rows_independent_of_T():

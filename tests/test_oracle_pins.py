@@ -416,6 +416,34 @@ def test_e4m3_decode_matches_spec_facts_and_torch():
     assert np.array_equal(np.nan_to_num(tab, nan=1e9), np.nan_to_num(t, nan=1e9))
 
 
+def test_e2m1_and_e8m0_decode_match_the_mx_spec():
+    """OCP Microscaling Formats v1.0: FP4 E2M1 magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    (max normal 6 = 1.5 * 2^2, min normal 1, min subnormal 0.5), sign in bit 3; the E8M0
+    scale is 2^(code - 127) with code 255 = NaN (checked against torch's float8_e8m0fnu)."""
+    import torch
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(oracle.E2M1_TABLE[:8]) == mags
+    assert list(oracle.E2M1_TABLE[8:]) == [-m for m in mags]
+    codes = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float32).numpy().astype(np.float64)
+    assert np.array_equal(oracle.e8m0_to_f64(codes), ref)
+    assert np.isnan(oracle.e8m0_to_f64(np.array([255], np.uint8)))[0]
+
+
+def test_mxfp4_dequant_layout_and_blocks():
+    """Packed layout (element 2j low nibble, 2j+1 high nibble of byte j) and one scale per
+    32 consecutive elements along K, on a hand-built matrix."""
+    packed = np.zeros((2, 32), np.uint8)          # 2 rows x 64 elements
+    packed[0, 0] = 0x2 | (0x7 << 4)               # row 0: e0 = 1.0, e1 = 6.0
+    packed[1, 20] = 0xB << 4                      # row 1: e41 = -1.5
+    scales = np.array([[127, 130], [126, 120]], np.uint8)   # 2^0, 2^3; 2^-1, 2^-7
+    v = oracle.dequant_mxfp4(packed, scales)
+    exp = np.zeros((2, 64))
+    exp[0, 0], exp[0, 1] = 1.0, 6.0
+    exp[1, 41] = -1.5 * 2.0 ** -7
+    assert np.array_equal(v, exp)
+
+
 def test_bf16_widening_matches_torch():
     import torch
     bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
