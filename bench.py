@@ -28,7 +28,9 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s + % of MI355X MFMA peak (prefill) / HBM GB/s (decode)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {1: 2500.0, 2: 5000.0, 0: 157.3}     # bf16, fp8, fp32 dense
+# dense peaks: bf16, fp8, fp32 (vector); MXFP4 weights meet E4M3 activations, an FP8 x FP4
+# product priced at the FP8 rate
+MFMA_PEAK_TFLOPS = {1: 2500.0, 2: 5000.0, 3: 5000.0, 0: 157.3}
 
 
 def log(*a):
@@ -151,13 +153,16 @@ def gate_up_roofline(w, T: int, n_active: int, gate_up_ms: float) -> dict:
     """Roofline of the grouped gate/up GEMM: algorithmic bytes (routed experts' gate/up
     weights, scales, x, the SwiGLU output) and flops per launch over its duration; the
     bound is whichever of the HBM and MFMA times is larger."""
-    from beam_inputs import DT_BF16, DT_FP8, DT_F32
+    from beam_inputs import DT_BF16, DT_FP8, DT_F32, DT_MXFP4
     P = T * w.K
-    wbytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[w.weight_dtype]
+    wbytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1, DT_MXFP4: 0.5}[w.weight_dtype]
+    abytes = {DT_F32: 4, DT_BF16: 2, DT_FP8: 1, DT_MXFP4: 1}[w.weight_dtype]   # the GEMM's A operand
     gate_up_weight_bytes = n_active * 2 * w.I * w.H * wbytes
     if w.weight_dtype == DT_FP8:
         gate_up_weight_bytes += n_active * (2 * w.I // 128) * (w.H // 128) * 4
-    gate_up_bytes = gate_up_weight_bytes + T * w.H * wbytes + P * w.I * 2
+    if w.weight_dtype == DT_MXFP4:
+        gate_up_weight_bytes += n_active * 2 * w.I * (w.H // 32)
+    gate_up_bytes = gate_up_weight_bytes + T * w.H * abytes + P * w.I * 2
     gate_up_flops = 2.0 * P * w.H * 2 * w.I
     peak_tf = MFMA_PEAK_TFLOPS[w.weight_dtype]
     t_hbm = gate_up_bytes / (HBM_PEAK_GBS * 1e9)
@@ -203,7 +208,7 @@ def main():
         for T in ts:
             r = layer.measure(T, args.steps, args.warmup)
             roof = gate_up_roofline(w, T, r["n_active"], r["kernel_ms"]["gate_up"])
-            wbytes = {0: 4, 1: 2, 2: 1}[w.weight_dtype]
+            wbytes = {0: 4, 1: 2, 2: 1, 3: 0.5}[w.weight_dtype]
             layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
             print(json.dumps({"sweep": w.name, "T": T, "ms_per_step": round(r["ms_per_step"], 4),
                               "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1),
@@ -222,7 +227,7 @@ def main():
 
     # ---- whole-layer figures ----
     P = w.T * w.K
-    wbytes = {0: 4, 1: 2, 2: 1}[w.weight_dtype]
+    wbytes = {0: 4, 1: 2, 2: 1, 3: 0.5}[w.weight_dtype]
     layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
     layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
     extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
@@ -282,7 +287,7 @@ def cpu_baseline(w, inp, n_tok):
         x32 = inp.x[:n]
     else:
         x32 = oracle.bf16_to_f32(inp.x[:n])
-    bank = oracle.ExpertBank(inp.w13, inp.w2, {0: "f32", 1: "bf16", 2: "fp8_e4m3"}[w.weight_dtype],
+    bank = oracle.ExpertBank(inp.w13, inp.w2, {0: "f32", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp4"}[w.weight_dtype],
                              inp.w13_scale, inp.w2_scale, w.fp8_block)
     log(f"[bench] timing the CPU oracle on {n} tokens ...")
     t0 = time.perf_counter()

@@ -60,7 +60,9 @@ typedef enum {
 typedef enum {
     BEAM_DTYPE_F32 = 0,
     BEAM_DTYPE_BF16 = 1,
-    BEAM_DTYPE_FP8_E4M3 = 2     /* OCP E4M3FN, block-scaled (power-of-two FP32 scales) */
+    BEAM_DTYPE_FP8_E4M3 = 2,    /* OCP E4M3FN, block-scaled (power-of-two FP32 scales) */
+    BEAM_DTYPE_MXFP4 = 3        /* OCP MX FP4 (E2M1 elements, E8M0 scale per 32 along K);
+                                   weights only, up to 256 tokens per call */
 } beam_dtype;
 
 /*
@@ -130,22 +132,28 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  *   w_router   device [H, E] FP32;  logit_bias, select_bias device [E] FP32 or NULL
  *              (as in beam_moe_route)
  *   w13        device [E, 2I, H] weight_dtype: rows 0..I-1 gate, rows I..2I-1 up,
- *              each row H-contiguous
- *   w13_scale  FP8 only: device [E, 2I/128, H/128] FP32 block scales (value =
- *              code * scale of its 128x128 tile); must be NULL otherwise.  Each
- *              scale must be a normal power of two (an E8M0 block exponent): above
- *              256 tokens the matrix cores apply only its exponent field.
- *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous)
- *   w2_scale   FP8 only: device [E, H/128, I/128] FP32 powers of two; NULL otherwise
+ *              each row H-contiguous (MXFP4: [E, 2I, H/2] bytes, element 2j of a
+ *              row in the low nibble of byte j, 2j+1 in the high nibble)
+ *   w13_scale  FP8: device [E, 2I/128, H/128] FP32 block scales (value = code *
+ *              scale of its 128x128 tile).  Each scale must be a normal power of two
+ *              (an E8M0 block exponent): above 256 tokens the matrix cores apply only
+ *              its exponent field.  MXFP4: device [E, 2I, H/32] uint8 E8M0 codes
+ *              (value = E2M1 element * 2^(code - 127) of its block of 32 along K).
+ *              NULL for F32 and BF16 weights.
+ *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous;
+ *              MXFP4: [E, H, I/2] bytes)
+ *   w2_scale   FP8: device [E, H/128, I/128] FP32 powers of two; MXFP4: [E, H, I/32]
+ *              uint8 E8M0; NULL otherwise
  *   y          device [T, H] act_dtype out
  *   ids_out    device [T, K] int32 out, or NULL;  weights_out device [T, K] FP32 or NULL
- * With FP8 weights the activations entering each GEMM are quantised on the GPU to E4M3
- * with one FP32 scale per row (the row's amax / 448).
+ * With FP8 or MXFP4 weights the activations entering each GEMM are quantised on the GPU
+ * to E4M3 with one FP32 scale per row (the row's amax / 448).  MXFP4 weights are
+ * supported up to 256 tokens per call (BEAM_ERR_UNSUPPORTED above).
  */
 int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x,
                      const float* w_router, const float* logit_bias,
                      const float* select_bias, const void* w13,
-                     const float* w13_scale, const void* w2, const float* w2_scale,
+                     const void* w13_scale, const void* w2, const void* w2_scale,
                      void* y, int32_t* ids_out, float* weights_out, void* ws,
                      size_t ws_bytes, void* stream);
 
@@ -169,8 +177,8 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
                               int32_t step_k, const float* w_router,
                               const float* logit_bias, const float* select_bias,
                               const void* w13,
-                              const float* w13_scale, const void* w2,
-                              const float* w2_scale, void* moe_out, int32_t* ids_out,
+                              const void* w13_scale, const void* w2,
+                              const void* w2_scale, void* moe_out, int32_t* ids_out,
                               float* weights_out, void* ws, size_t ws_bytes, void* stream);
 
 /*

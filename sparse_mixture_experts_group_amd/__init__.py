@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbeam_moe.so")
 
 BEAM_OK, BEAM_ERR_INVALID_ARG, BEAM_ERR_UNSUPPORTED, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = range(5)
-BEAM_DTYPE_F32, BEAM_DTYPE_BF16, BEAM_DTYPE_FP8_E4M3 = range(3)
+BEAM_DTYPE_F32, BEAM_DTYPE_BF16, BEAM_DTYPE_FP8_E4M3, BEAM_DTYPE_MXFP4 = range(4)
 
 C_FUNCTIONS = ("beam_moe_status_string", "beam_moe_abi_version", "beam_moe_workspace_size",
                "beam_moe_workspace_map", "beam_moe_route", "beam_moe_forward",

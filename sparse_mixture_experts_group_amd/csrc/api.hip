@@ -30,7 +30,7 @@ bool config_valid(const beam_moe_config* c) {
     if (c->topk < 1 || c->topk > kMaxTopK || c->topk > c->topk_groups * S) return false;
     if (!isfinite(c->routed_scale)) return false;
     if (c->act_dtype < BEAM_DTYPE_F32 || c->act_dtype > BEAM_DTYPE_FP8_E4M3) return false;
-    if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_FP8_E4M3) return false;
+    if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_MXFP4) return false;
     if (!(c->norm_eps >= 0.0f) || !isfinite(c->norm_eps)) return false;
     return true;
 }
@@ -40,7 +40,8 @@ bool config_supported(const beam_moe_config* c) {
     const int a = c->act_dtype, w = c->weight_dtype;
     const bool pair_ok = (a == BEAM_DTYPE_F32 && w == BEAM_DTYPE_F32) ||
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_BF16) ||
-                         (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_FP8_E4M3);
+                         (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_FP8_E4M3) ||
+                         (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_MXFP4);
     if (!pair_ok) return false;
     if (c->hidden > 16384) return false;   // LDS staging of the small-batch router kernel
     if (w == BEAM_DTYPE_F32) {
@@ -68,7 +69,8 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     const int64_t E = c.n_experts, K = c.topk, H = c.hidden, I = c.inter;
     const int64_t P = T * K;
     const bool f32 = c.weight_dtype == BEAM_DTYPE_F32;
-    const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3;
+    // FP8 and MXFP4 weights take E4M3 activations (row-scaled copies of x and h)
+    const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3 || c.weight_dtype == BEAM_DTYPE_MXFP4;
     const bool bf16_act = c.act_dtype == BEAM_DTYPE_BF16;
     L.nblk = static_cast<int>((T + kSelectTokens - 1) / kSelectTokens);
     L.bm = kPrefillBM;
@@ -205,7 +207,7 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
 // Expert GEMMs: x_exp [T, H] in the weights' activation format -> yperm [T*K, H].
 void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
                  const void* x_exp, const float* x_exp_scale, const void* w13,
-                 const float* w13_scale, const void* w2, const float* w2_scale,
+                 const void* w13_scale, const void* w2, const void* w2_scale,
                  const int32_t* ids) {
     const int64_t P = T * c.topk;
     const int H = c.hidden, I = c.inter;
@@ -234,7 +236,7 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
             if (decode) launch_gemm_bf16_decode(st, kDown, g2);
             else launch_gemm_prefill(st, kDown, g2, false);
         }
-    } else {
+    } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) launch_gemm_fp8_decode(st, kGateUp, g1);
@@ -247,6 +249,11 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
             if (decode) launch_gemm_fp8_decode(st, kDown, g2);
             else launch_gemm_prefill(st, kDown, g2, true);
         }
+    } else {            // MXFP4 weights (streaming kernels only; larger T is rejected up front)
+        { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_mxfp4_decode(st, kGateUp, g1); }
+        launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
+        g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
+        { Bracket b(BEAM_KERNEL_DOWN, st); launch_gemm_mxfp4_decode(st, kDown, g2); }
     }
 }
 
@@ -304,26 +311,29 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const f
     return launch_status();
 }
 
-static int check_weights(const beam_moe_config* cfg, const void* w13, const float* w13_scale, const void* w2,
-                         const float* w2_scale) {
+static int check_weights(const beam_moe_config* cfg, int64_t T, const void* w13, const void* w13_scale,
+                         const void* w2, const void* w2_scale) {
     if (!w13 || !w2) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(w13) || !aligned16(w2)) return BEAM_ERR_INVALID_ARG;
-    const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3;
-    if (fp8 != (w13_scale != nullptr) || fp8 != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
+    const bool scaled = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4;
+    if (scaled != (w13_scale != nullptr) || scaled != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
+    if (scaled && (!aligned16(w13_scale) || !aligned16(w2_scale))) return BEAM_ERR_INVALID_ARG;
+    // MXFP4 weights have streaming kernels only (up to the streaming range of tokens)
+    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > kDecodeMaxT) return BEAM_ERR_UNSUPPORTED;
     return BEAM_OK;
 }
 
 int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
                      const float* logit_bias, const float* select_bias, const void* w13,
-                     const float* w13_scale, const void* w2,
-                     const float* w2_scale, void* y, int32_t* ids_out, float* weights_out, void* ws,
+                     const void* w13_scale, const void* w2,
+                     const void* w2_scale, void* y, int32_t* ids_out, float* weights_out, void* ws,
                      size_t ws_bytes, void* stream) {
     int s = check_common(cfg, T);
     if (s != BEAM_OK) return s;
     if (T == 0) return BEAM_OK;
     if (!x || !w_router || !y) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(y)) return BEAM_ERR_INVALID_ARG;
-    if ((s = check_weights(cfg, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
+    if ((s = check_weights(cfg, T, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
     if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
@@ -334,7 +344,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
     run_router(*cfg, T, L, ws, st, x, bf16_act, w_router, logit_bias, select_bias, ids, wts, true);
     const void* x_exp = x;
     const float* x_exp_scale = nullptr;
-    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3) {
+    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4) {
         launch_quant_rows_fp8(st, T, cfg->hidden, true, x, at<uint8_t>(ws, L.x8), at<float>(ws, L.x8s));
         x_exp = at<void>(ws, L.x8);
         x_exp_scale = at<float>(ws, L.x8s);
@@ -349,8 +359,8 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
 int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, const float* pre_gain,
                               const float* post_gain, int32_t step_k, const float* w_router,
                               const float* logit_bias, const float* select_bias, const void* w13,
-                              const float* w13_scale,
-                              const void* w2, const float* w2_scale, void* moe_out, int32_t* ids_out,
+                              const void* w13_scale,
+                              const void* w2, const void* w2_scale, void* moe_out, int32_t* ids_out,
                               float* weights_out, void* ws, size_t ws_bytes, void* stream) {
     int s = check_common(cfg, T);
     if (s != BEAM_OK) return s;
@@ -359,14 +369,15 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, co
     if (T == 0) return BEAM_OK;
     if (!h || !w_router) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(h) || !aligned16(w_router) || (moe_out && !aligned16(moe_out))) return BEAM_ERR_INVALID_ARG;
-    if ((s = check_weights(cfg, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
+    if ((s = check_weights(cfg, T, w13, w13_scale, w2, w2_scale)) != BEAM_OK) return s;
     if ((s = check_ws(cfg, T, ws, ws_bytes)) != BEAM_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Layout L = make_layout(*cfg, T);
     clear_hip_error();
     int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
     float* wts = weights_out ? weights_out : at<float>(ws, L.wts);
-    const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3;
+    // E4M3 activations for FP8 and MXFP4 weights
+    const bool fp8 = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4;
     const int H = cfg->hidden;
     launch_prenorm(st, T, H, static_cast<const uint16_t*>(h), pre_gain, cfg->norm_eps, at<float>(ws, L.xhat32),
                    fp8 ? nullptr : at<uint16_t>(ws, L.x16), fp8 ? at<uint8_t>(ws, L.x8) : nullptr,

@@ -47,8 +47,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
     const int kb_n = g.kd / 128;
     const uint8_t* wp = static_cast<const uint8_t*>(g.w) + (static_cast<int64_t>(e) * nw + n0 + ln) * g.kd + lq * 32;
     const uint8_t* wu = wp + static_cast<int64_t>(g.n_out) * g.kd;
-    const float* swg = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + n0 / 128) * kb_n;
-    const float* swu = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + n0) / 128) * kb_n;
+    const float* wsc = static_cast<const float*>(g.w_scale);      // FP32 block scales
+    const float* swg = wsc + (static_cast<int64_t>(e) * (nw / 128) + n0 / 128) * kb_n;
+    const float* swu = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + n0) / 128) * kb_n;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 
     // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up

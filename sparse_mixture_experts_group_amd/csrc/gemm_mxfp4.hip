@@ -1,0 +1,175 @@
+// MXFP4 expert weights (OCP Microscaling Formats v1.0: FP4 E2M1 elements, one E8M0
+// scale per 32 consecutive values along K) with E4M3 activations (one FP32 scale per
+// row), for few rows per expert (decode): the grouped GEMM is a weight stream, as in the
+// BF16 and FP8 streaming kernels, on v_mfma_scale_f32_16x16x128_f8f6f4 with an FP4 B
+// operand.  The matrix core applies each weight block's E8M0 scale itself (one scale
+// byte per lane), so the accumulation runs straight through K in FP32; the row scale of
+// the activations is applied in the epilogue.
+//
+// SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
+// routed per token"; FP32 SwiGLU product per the "Residual stream" section):
+//   gate/up:  h[r, j] = SiLU(a_r . Wg[j]) * (a_r . Wu[j])   (a_r gathered by token)
+//   down:     y[r, n] = h_r . Wd[n]
+//
+// Operand layout of the 16x16x128 f8f6f4 MFMA with FP8 A and FP4 B (measured on gfx950):
+// lane l = 16 q + c of the FP4 operand holds column c, K values 32 q .. 32 q + 31 (16
+// bytes, element 2j in the low nibble of byte j), and its scale byte covers exactly those
+// 32 values -- one MX block; the FP8 operand lane l = 16 q + r pairs with it when it holds
+// row r, K values 16 q .. 16 q + 15 in bytes 0-15 and 64 + 16 q .. 64 + 16 q + 15 in
+// bytes 16-31.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace beam {
+
+namespace {
+constexpr int kUnitScale = 0x7f;      // E8M0 code of 2^0
+
+__device__ __forceinline__ i32x8 join_a(u32x4 lo, u32x4 hi) {
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+__device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
+    i32x8 r;
+    r[0] = v[0]; r[1] = v[1]; r[2] = v[2]; r[3] = v[3];
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma_a8w4(i32x8 a, i32x8 b, int scale_b, f32x4 c) {
+    // format codes: A 0 = FP8 E4M3, B 4 = FP4 E2M1
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, kUnitScale, 0, scale_b);
+}
+}  // namespace
+
+// One block per (active expert, 64 output columns for gate/up, 128 for down); each wave
+// streams 32 weight rows (16 gate + 16 up, or 32 down rows) with U 128-wide K blocks of
+// loads in flight, and the expert's activation rows ride along as A, 16 R per pass.
+template <int MODE, bool GATHER, int U, int R>
+__global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
+    const int slot = blockIdx.y;
+    if (slot >= g.meta[kMetaActive]) return;
+    const int e = g.active[slot];
+    const int rows = g.exp_cnt[e], row0 = g.exp_off[e];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int WC = (MODE == kGateUp) ? 16 : 32;
+    const int n0 = (blockIdx.x * 4 + wave) * WC;
+    if (n0 >= g.n_out) return;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
+    const int64_t wrow_b = g.kd / 2, srow_b = g.kd / 32;       // bytes per weight / scale row
+    const int64_t r_first = static_cast<int64_t>(e) * nw + n0 + ln;
+    const int64_t r_second = r_first + ((MODE == kGateUp) ? g.n_out : 16);
+    const uint8_t* w = static_cast<const uint8_t*>(g.w);
+    const uint8_t* sc = static_cast<const uint8_t*>(g.w_scale);      // E8M0 codes
+    const uint8_t* wp0 = w + r_first * wrow_b + lq * 16;
+    const uint8_t* wp1 = w + r_second * wrow_b + lq * 16;
+    const uint8_t* sp0 = sc + r_first * srow_b;
+    const uint8_t* sp1 = sc + r_second * srow_b;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+
+    for (int m0 = 0; m0 < rows; m0 += 16 * R) {
+        bool mv[R];
+        const uint8_t* ap[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = m0 + 16 * r + ln;
+            mv[r] = m < rows;
+            const int mr = mv[r] ? m : rows - 1;
+            const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
+            ap[r] = static_cast<const uint8_t*>(g.a) + arow * g.lda + lq * 16;
+        }
+        f32x4 acc0[R], acc1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+        for (int k = 0; k < g.kd; k += 128 * U) {
+            u32x4 b0[U], b1[U], a[R][U][2];
+            // E8M0 scales of blocks k/32 + 4u + lq: byte lq of dword u of 4U bytes
+            uint32_t s0[U], s1[U];
+            if constexpr (U % 4 == 0) {
+#pragma unroll
+                for (int v = 0; v < U / 4; ++v) {
+                    const u32x4 v0 = *reinterpret_cast<const u32x4*>(sp0 + k / 32 + 16 * v);
+                    const u32x4 v1 = *reinterpret_cast<const u32x4*>(sp1 + k / 32 + 16 * v);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { s0[4 * v + u] = v0[u]; s1[4 * v + u] = v1[u]; }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    s0[u] = *reinterpret_cast<const uint32_t*>(sp0 + k / 32 + 4 * u);
+                    s1[u] = *reinterpret_cast<const uint32_t*>(sp1 + k / 32 + 4 * u);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                b0[u] = *reinterpret_cast<const u32x4*>(wp0 + (k + 128 * u) / 2);
+                b1[u] = *reinterpret_cast<const u32x4*>(wp1 + (k + 128 * u) / 2);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    a[r][u][0] = u32x4{0u, 0u, 0u, 0u};
+                    a[r][u][1] = u32x4{0u, 0u, 0u, 0u};
+                    if (mv[r]) {
+                        a[r][u][0] = *reinterpret_cast<const u32x4*>(ap[r] + k + 128 * u);
+                        a[r][u][1] = *reinterpret_cast<const u32x4*>(ap[r] + k + 128 * u + 64);
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sc0 = static_cast<int>((s0[u] >> (8 * lq)) & 0xffu);
+                const int sc1 = static_cast<int>((s1[u] >> (8 * lq)) & 0xffu);
+                const i32x8 bb0 = fp4_operand(b0[u]), bb1 = fp4_operand(b1[u]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const i32x8 av = join_a(a[r][u][0], a[r][u][1]);
+                    acc0[r] = mfma_a8w4(av, bb0, sc0, acc0[r]);
+                    acc1[r] = mfma_a8w4(av, bb1, sc1, acc1[r]);
+                }
+            }
+        }
+        // C[m = lq*4 + i][n = ln] of row tile r
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mm = m0 + 16 * r + lq * 4 + i;
+                if (mm >= rows) continue;
+                const int64_t ar = GATHER ? g.pair_of_row[row0 + mm] / g.topk : static_cast<int64_t>(row0 + mm);
+                const float sa = g.a_scale[ar];
+                uint16_t* orow = out + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
+                if (MODE == kGateUp) {
+                    orow[0] = f32_to_bf16_bits(silu(acc0[r][i] * sa) * (acc1[r][i] * sa));
+                } else {
+                    orow[0] = f32_to_bf16_bits(acc0[r][i] * sa);
+                    orow[16] = f32_to_bf16_bits(acc1[r][i] * sa);
+                }
+            }
+    }
+}
+
+void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return;
+    const int cols_per_block = (mode == kGateUp) ? 64 : 128;     // n_out is a multiple of 32
+    dim3 grid((g.n_out + cols_per_block - 1) / cols_per_block, g.max_active);
+    const bool u8 = (g.kd % 1024) == 0;
+    const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
+#define BEAM_DEC(M, GA, U) \
+    do { if (r2) gemm_mxfp4_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
+         else gemm_mxfp4_decode<M, GA, U, 1><<<grid, 256, 0, st>>>(g); } while (0)
+    if (mode == kGateUp) {
+        if (g.gather) { if (u8) BEAM_DEC(kGateUp, true, 8); else BEAM_DEC(kGateUp, true, 1); }
+        else          { if (u8) BEAM_DEC(kGateUp, false, 8); else BEAM_DEC(kGateUp, false, 1); }
+    } else {
+        if (g.gather) { if (u8) BEAM_DEC(kDown, true, 8); else BEAM_DEC(kDown, true, 1); }
+        else          { if (u8) BEAM_DEC(kDown, false, 8); else BEAM_DEC(kDown, false, 1); }
+    }
+#undef BEAM_DEC
+}
+
+}  // namespace beam

@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         const int kb_n = g.kd / 128;
         const float* r_lo;
         const float* r_hi;
+        const float* wsc = static_cast<const float*>(g.w_scale);
         if (MODE == kGateUp) {
-            r_lo = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_n;
-            r_hi = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_n;
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_n;
+            r_hi = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_n;
         } else {
-            r_lo = g.w_scale + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_n;
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_n;
             r_hi = r_lo;
         }
         const int l = min(lane, kb_n - 1);

@@ -68,7 +68,7 @@ struct GroupedGemmArgs {
     int topk;
     const float* a_scale;     // FP8: [rows or T, Kd/128] activation scales, else null
     const void* w;            // [E, Nw, Kd] expert weights
-    const float* w_scale;     // FP8: [E, Nw/128, Kd/128], else null
+    const void* w_scale;      // FP8: FP32 [E, Nw/128, Kd/128]; MXFP4: E8M0 bytes [E, Nw, Kd/32]; else null
     int n_out;                // output columns (I for gate/up, H for down)
     int kd;                   // reduction length
     const int32_t* exp_cnt;   // [E]
@@ -90,6 +90,8 @@ void launch_gemm_f32(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, in
 // gemm_bf16_decode.hip / gemm_fp8.hip: few rows per expert, weight streaming
 void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// gemm_mxfp4.hip: MXFP4 weights, E4M3 activations, weight streaming
+void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 // gemm_prefill.hip: 256 x 256 LDS-tiled MFMA, BF16 or FP8 operands
 void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8);
 

@@ -9,12 +9,14 @@ import torch
 
 import oracle
 import sparse_mixture_experts_group_amd as bm
-from beam_inputs import DT_BF16, DT_F32, DT_FP8, DTYPE_NAMES, WORKLOADS
+from beam_inputs import DT_BF16, DT_F32, DT_FP8, DT_MXFP4, DTYPE_NAMES, WORKLOADS
 from conftest import gpu_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {DT_F32: 1e-5, DT_BF16: 2e-2, DT_FP8: 6e-2}
+# MXFP4 weights are exact as stored on both sides; the GPU error is the E4M3 activation
+# quantisation, as on the FP8 path
+TOL = {DT_F32: 1e-5, DT_BF16: 2e-2, DT_FP8: 6e-2, DT_MXFP4: 6e-2}
 
 
 def cfg_of(w):
@@ -289,3 +291,24 @@ def test_fp8_forward(T):
     err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
     print(f"[case] fp8 forward T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[DT_FP8]
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 experts (E2M1 weights with E8M0 block scales, E4M3 activations)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [16, 200])
+def test_mxfp4_forward(T):
+    """MXFP4 experts through beam_moe_forward (streaming kernels, 16 or 32 rows per
+    pass) against the oracle on the stored FP4 weights, every token."""
+    w, full, dev, x, bias = gpu_inputs("beam_decode_mxfp4_t16", T)
+    print(f"[case] mxfp4 forward T={T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, bias)
+    x32 = oracle.bf16_to_f32(x)
+    z = oracle.router_logits(x32, full.w_router, bias)
+    rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, rid, rw)
+    check_permutation(w, ws, ids)
+    yref = oracle.moe_combine(x32.astype(np.float64), rid, rw, bank_of(w, full))
+    err = rel_inf(y.float().cpu().numpy().astype(np.float64), yref)
+    print(f"[case] mxfp4 forward T={T} rel_inf={err:.3e}", flush=True)
+    assert err <= TOL[DT_MXFP4]
