@@ -24,6 +24,8 @@ namespace beam {
 
 namespace {
 constexpr int kUnitScale = 0x7f;      // E8M0 code of 2^0
+constexpr int kMxfp4Streams = 2;      // 16-row weight streams per wave
+constexpr int kMxfp4U = 8;            // 128-wide K blocks per iteration
 
 __device__ __forceinline__ i32x8 join_a(u32x4 lo, u32x4 hi) {
     i32x8 r;
@@ -45,30 +47,36 @@ __device__ __forceinline__ f32x4 mfma_a8w4(i32x8 a, i32x8 b, int scale_b, f32x4 
 }
 }  // namespace
 
-// One block per (active expert, 64 output columns for gate/up, 128 for down); each wave
-// streams 32 weight rows (16 gate + 16 up, or 32 down rows) with U 128-wide K blocks of
-// loads in flight, and the expert's activation rows ride along as A, 16 R per pass.
-template <int MODE, bool GATHER, int U, int R>
+// One block per (active expert, 64 NS/2 output columns for gate/up, 64 NS for down);
+// each wave streams NS groups of 16 weight rows (gate/up: NS/2 pairs of 16 gate + 16 up
+// rows; down: NS x 16 consecutive rows) with U 128-wide K blocks of loads in flight, and
+// the expert's activation rows ride along as A, 16 R per pass.
+template <int MODE, bool GATHER, int U, int R, int NS>
 __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
     const int slot = blockIdx.y;
     if (slot >= g.meta[kMetaActive]) return;
     const int e = g.active[slot];
     const int rows = g.exp_cnt[e], row0 = g.exp_off[e];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    constexpr int WC = (MODE == kGateUp) ? 16 : 32;
+    constexpr int WC = (MODE == kGateUp) ? 8 * NS : 16 * NS;     // output columns per wave
     const int n0 = (blockIdx.x * 4 + wave) * WC;
     if (n0 >= g.n_out) return;
     const int ln = lane & 15, lq = lane >> 4;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const int64_t wrow_b = g.kd / 2, srow_b = g.kd / 32;       // bytes per weight / scale row
-    const int64_t r_first = static_cast<int64_t>(e) * nw + n0 + ln;
-    const int64_t r_second = r_first + ((MODE == kGateUp) ? g.n_out : 16);
     const uint8_t* w = static_cast<const uint8_t*>(g.w);
     const uint8_t* sc = static_cast<const uint8_t*>(g.w_scale);      // E8M0 codes
-    const uint8_t* wp0 = w + r_first * wrow_b + lq * 16;
-    const uint8_t* wp1 = w + r_second * wrow_b + lq * 16;
-    const uint8_t* sp0 = sc + r_first * srow_b;
-    const uint8_t* sp1 = sc + r_second * srow_b;
+    const uint8_t* wp[NS];
+    const uint8_t* sp[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+        // gate/up: stream 2j = gate rows of columns n0 + 16 j, 2j + 1 = their up rows
+        const int64_t rr = (MODE == kGateUp)
+            ? static_cast<int64_t>(e) * nw + n0 + 16 * (t >> 1) + ln + ((t & 1) ? g.n_out : 0)
+            : static_cast<int64_t>(e) * nw + n0 + 16 * t + ln;
+        wp[t] = w + rr * wrow_b + lq * 16;
+        sp[t] = sc + rr * srow_b;
+    }
     uint16_t* out = static_cast<uint16_t*>(g.out);
 
     for (int m0 = 0; m0 < rows; m0 += 16 * R) {
@@ -82,32 +90,30 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
             const int64_t arow = GATHER ? g.pair_of_row[row0 + mr] / g.topk : static_cast<int64_t>(row0 + mr);
             ap[r] = static_cast<const uint8_t*>(g.a) + arow * g.lda + lq * 16;
         }
-        f32x4 acc0[R], acc1[R];
+        f32x4 acc[R][NS];
 #pragma unroll
-        for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NS; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k = 0; k < g.kd; k += 128 * U) {
-            u32x4 b0[U], b1[U], a[R][U][2];
+            u32x4 b[NS][U], a[R][U][2];
             // E8M0 scales of blocks k/32 + 4u + lq: byte lq of dword u of 4U bytes
-            uint32_t s0[U], s1[U];
-            if constexpr (U % 4 == 0) {
+            uint32_t s[NS][U];
 #pragma unroll
-                for (int v = 0; v < U / 4; ++v) {
-                    const u32x4 v0 = *reinterpret_cast<const u32x4*>(sp0 + k / 32 + 16 * v);
-                    const u32x4 v1 = *reinterpret_cast<const u32x4*>(sp1 + k / 32 + 16 * v);
+            for (int t = 0; t < NS; ++t) {
+                if constexpr (U % 4 == 0) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) { s0[4 * v + u] = v0[u]; s1[4 * v + u] = v1[u]; }
+                    for (int v = 0; v < U / 4; ++v) {
+                        const u32x4 sv = *reinterpret_cast<const u32x4*>(sp[t] + k / 32 + 16 * v);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) s[t][4 * v + u] = sv[u];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) s[t][u] = *reinterpret_cast<const uint32_t*>(sp[t] + k / 32 + 4 * u);
                 }
-            } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    s0[u] = *reinterpret_cast<const uint32_t*>(sp0 + k / 32 + 4 * u);
-                    s1[u] = *reinterpret_cast<const uint32_t*>(sp1 + k / 32 + 4 * u);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                b0[u] = *reinterpret_cast<const u32x4*>(wp0 + (k + 128 * u) / 2);
-                b1[u] = *reinterpret_cast<const u32x4*>(wp1 + (k + 128 * u) / 2);
+                for (int u = 0; u < U; ++u) b[t][u] = *reinterpret_cast<const u32x4*>(wp[t] + (k + 128 * u) / 2);
             }
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -122,14 +128,13 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
                 }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int sc0 = static_cast<int>((s0[u] >> (8 * lq)) & 0xffu);
-                const int sc1 = static_cast<int>((s1[u] >> (8 * lq)) & 0xffu);
-                const i32x8 bb0 = fp4_operand(b0[u]), bb1 = fp4_operand(b1[u]);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const i32x8 av = join_a(a[r][u][0], a[r][u][1]);
-                    acc0[r] = mfma_a8w4(av, bb0, sc0, acc0[r]);
-                    acc1[r] = mfma_a8w4(av, bb1, sc1, acc1[r]);
+                for (int t = 0; t < NS; ++t) {
+                    const int scb = static_cast<int>((s[t][u] >> (8 * lq)) & 0xffu);
+                    const i32x8 bb = fp4_operand(b[t][u]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r][t] = mfma_a8w4(join_a(a[r][u][0], a[r][u][1]), bb, scb, acc[r][t]);
                 }
             }
         }
@@ -144,10 +149,12 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
                 const float sa = g.a_scale[ar];
                 uint16_t* orow = out + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
                 if (MODE == kGateUp) {
-                    orow[0] = f32_to_bf16_bits(silu(acc0[r][i] * sa) * (acc1[r][i] * sa));
+#pragma unroll
+                    for (int j = 0; j < NS / 2; ++j)
+                        orow[16 * j] = f32_to_bf16_bits(silu(acc[r][2 * j][i] * sa) * (acc[r][2 * j + 1][i] * sa));
                 } else {
-                    orow[0] = f32_to_bf16_bits(acc0[r][i] * sa);
-                    orow[16] = f32_to_bf16_bits(acc1[r][i] * sa);
+#pragma unroll
+                    for (int t = 0; t < NS; ++t) orow[16 * t] = f32_to_bf16_bits(acc[r][t][i] * sa);
                 }
             }
     }
@@ -155,20 +162,26 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
 
 void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
     if (g.max_active == 0) return;
-    const int cols_per_block = (mode == kGateUp) ? 64 : 128;     // n_out is a multiple of 32
+    constexpr int NS = kMxfp4Streams;
+    const int cols_per_block = 4 * ((mode == kGateUp) ? 8 * NS : 16 * NS);   // n_out: multiple of it
     dim3 grid((g.n_out + cols_per_block - 1) / cols_per_block, g.max_active);
-    const bool u8 = (g.kd % 1024) == 0;
+    // K blocks of 128 per iteration: as many as divide the reduction
+    const int u = (g.kd % (128 * kMxfp4U) == 0) ? kMxfp4U : ((g.kd % 512 == 0) ? 4 : 1);
     const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
-#define BEAM_DEC(M, GA, U) \
-    do { if (r2) gemm_mxfp4_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
-         else gemm_mxfp4_decode<M, GA, U, 1><<<grid, 256, 0, st>>>(g); } while (0)
+#define BEAM_DEC_U(M, GA, U) \
+    do { if (r2) gemm_mxfp4_decode<M, GA, U, 2, NS><<<grid, 256, 0, st>>>(g); \
+         else gemm_mxfp4_decode<M, GA, U, 1, NS><<<grid, 256, 0, st>>>(g); } while (0)
+#define BEAM_DEC(M, GA) \
+    do { if (u == kMxfp4U) BEAM_DEC_U(M, GA, kMxfp4U); else if (u == 4) BEAM_DEC_U(M, GA, 4); \
+         else BEAM_DEC_U(M, GA, 1); } while (0)
     if (mode == kGateUp) {
-        if (g.gather) { if (u8) BEAM_DEC(kGateUp, true, 8); else BEAM_DEC(kGateUp, true, 1); }
-        else          { if (u8) BEAM_DEC(kGateUp, false, 8); else BEAM_DEC(kGateUp, false, 1); }
+        if (g.gather) BEAM_DEC(kGateUp, true);
+        else BEAM_DEC(kGateUp, false);
     } else {
-        if (g.gather) { if (u8) BEAM_DEC(kDown, true, 8); else BEAM_DEC(kDown, true, 1); }
-        else          { if (u8) BEAM_DEC(kDown, false, 8); else BEAM_DEC(kDown, false, 1); }
+        if (g.gather) BEAM_DEC(kDown, true);
+        else BEAM_DEC(kDown, false);
     }
+#undef BEAM_DEC_U
 #undef BEAM_DEC
 }
 
