@@ -213,9 +213,11 @@ WORKLOADS = {
     # full sublayer with FP8 experts
     "beam_sublayer_fp8_t8192": Workload("beam_sublayer_fp8_t8192", T=8192, H=5120, I=2560, E=256, G=8,
                                         Kg=4, K=8, weight_dtype=DT_FP8, sublayer=True),
-    # decode batch with MXFP4 experts (E2M1 elements, E8M0 scale per 32 along K)
+    # MXFP4 experts (E2M1 elements, E8M0 scale per 32 along K): decode batch and prefill
     "beam_decode_mxfp4_t16": Workload("beam_decode_mxfp4_t16", T=16, H=5120, I=2560, E=256, G=8, Kg=4, K=8,
                                       weight_dtype=DT_MXFP4, x_recipe="rms_normal"),
+    "beam_prefill_mxfp4_t4096": Workload("beam_prefill_mxfp4_t4096", T=4096, H=5120, I=2560, E=256, G=8, Kg=4,
+                                         K=8, weight_dtype=DT_MXFP4),
 }
 
 

@@ -228,32 +228,40 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) launch_gemm_bf16_decode(st, kGateUp, g1);
-            else launch_gemm_prefill(st, kGateUp, g1, false);
+            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kBf16);
         }
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) launch_gemm_bf16_decode(st, kDown, g2);
-            else launch_gemm_prefill(st, kDown, g2, false);
+            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kBf16);
         }
     } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) launch_gemm_fp8_decode(st, kGateUp, g1);
-            else launch_gemm_prefill(st, kGateUp, g1, true);
+            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kFp8);
         }
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) launch_gemm_fp8_decode(st, kDown, g2);
-            else launch_gemm_prefill(st, kDown, g2, true);
+            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kFp8);
         }
-    } else {            // MXFP4 weights (streaming kernels only; larger T is rejected up front)
-        { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_mxfp4_decode(st, kGateUp, g1); }
+    } else {            // MXFP4 weights
+        {
+            Bracket b(BEAM_KERNEL_GATE_UP, st);
+            if (decode) launch_gemm_mxfp4_decode(st, kGateUp, g1);
+            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kMxfp4);
+        }
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
-        { Bracket b(BEAM_KERNEL_DOWN, st); launch_gemm_mxfp4_decode(st, kDown, g2); }
+        {
+            Bracket b(BEAM_KERNEL_DOWN, st);
+            if (decode) launch_gemm_mxfp4_decode(st, kDown, g2);
+            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kMxfp4);
+        }
     }
 }
 
@@ -318,8 +326,10 @@ static int check_weights(const beam_moe_config* cfg, int64_t T, const void* w13,
     const bool scaled = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4;
     if (scaled != (w13_scale != nullptr) || scaled != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
     if (scaled && (!aligned16(w13_scale) || !aligned16(w2_scale))) return BEAM_ERR_INVALID_ARG;
-    // MXFP4 weights have streaming kernels only (up to the streaming range of tokens)
-    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > kDecodeMaxT) return BEAM_ERR_UNSUPPORTED;
+    // above the streaming range, MXFP4 tiles stage their weight scales in LDS
+    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > kDecodeMaxT &&
+        (cfg->hidden > kMxfp4PrefillMaxKd || cfg->inter > kMxfp4PrefillMaxKd))
+        return BEAM_ERR_UNSUPPORTED;
     return BEAM_OK;
 }
 

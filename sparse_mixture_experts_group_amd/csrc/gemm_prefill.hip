@@ -1,5 +1,6 @@
 // Grouped expert GEMMs for many rows per expert (prefill-sized batches) on the gfx950
-// matrix cores, FP32 accumulation, BF16 or FP8 (OCP E4M3FN) operands.
+// matrix cores, FP32 accumulation; BF16, FP8 (OCP E4M3FN) or MXFP4 (OCP MX: FP4 E2M1
+// elements with an E8M0 scale per 32 along K) weights.
 //
 // SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
 // routed per token"; FP32 SwiGLU product per the "Residual stream" section):
@@ -16,8 +17,10 @@
 //
 // FP8: weights carry one power-of-two scale per 128 x 128 block, which the f8f6f4 MFMA
 // applies itself as the E8M0 scale of its B operand (the FP32 scale's exponent field is
-// the E8M0 code), so the accumulation needs no per-block fold.  Activations carry one
-// FP32 scale per row, applied in the epilogue.
+// the E8M0 code), so the accumulation needs no per-block fold.  MXFP4: the FP4 B
+// operand of a lane holds one 32-value MX block of its column, whose E8M0 scale is the
+// lane's B scale byte; the block's scales are staged in LDS once.  Activations (FP8 and
+// MXFP4 weights) are E4M3 with one FP32 scale per row, applied in the epilogue.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -25,13 +28,24 @@ namespace beam {
 
 namespace {
 constexpr int kUnitScale = 0x7f;                // E8M0 code of 2^0
+enum : int { kWtBf16 = 0, kWtFp8 = 1, kWtMxfp4 = 2 };
 
-// K advances 64 bytes per LDS stage (32 BF16 or 64 FP8 values); A (256 rows) and B
-// (256 rows) take 32 KB per stage.
-constexpr int kStageBytes = (kPrefillBM + 256) * kStageRowBytes;
+// K advances per LDS stage: A rows hold 64 bytes (32 BF16 or 64 E4M3
+// values), B rows 64 bytes (BF16, FP8) or 32 bytes (64 packed FP4 values).
+template <int WT> constexpr int b_row_bytes() { return WT == kWtMxfp4 ? 32 : kStageRowBytes; }
+template <int WT> constexpr int stage_bytes() { return kPrefillBM * kStageRowBytes + 256 * b_row_bytes<WT>(); }
 constexpr int kStages = 4;
-constexpr size_t kLdsBytes = kStages * kStageBytes;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+constexpr int kMxfp4MaxKd = 8192;               // LDS holds the block's 256 x kd/32 scales
+template <int WT> constexpr size_t lds_bytes_max() {
+    return kStages * stage_bytes<WT>() + (WT == kWtMxfp4 ? 256 * (kMxfp4MaxKd / 32) : 0);
+}
+static_assert(lds_bytes_max<kWtBf16>() <= 160 * 1024 && lds_bytes_max<kWtMxfp4>() <= 160 * 1024, "LDS budget");
+
+// FP4 rows of 32 bytes: chunk c of row r in slot c ^ ((r >> 3) & 1), so the 16 rows one
+// fragment read serves per LDS cycle cover all banks.
+__device__ __forceinline__ int fp4_offset(int row, int chunk) {
+    return row * 32 + ((chunk ^ ((row >> 3) & 1)) << 4);
+}
 
 __device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
     i32x8 r;
@@ -40,11 +54,20 @@ __device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
     return r;
 }
 
+__device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
+    i32x8 r;
+    r[0] = v[0]; r[1] = v[1]; r[2] = v[2]; r[3] = v[3];
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
 // Fragments of one LDS stage for one wave: BF16 - two 16-wide K steps of 8 values per
-// lane; FP8 - one 64-wide K step of 32 values per lane.
-template <bool FP8> struct StageFrags;
-template <> struct StageFrags<false> { bf16x8 a[2][4]; bf16x8 b[2][4]; };
-template <> struct StageFrags<true> { i32x8 a[4]; i32x8 b[4]; };
+// lane; FP8 - one 64-wide K step of 32 values per lane; MXFP4 - A as FP8, B 32 FP4
+// values (16 bytes) per lane.
+template <int WT> struct StageFrags;
+template <> struct StageFrags<kWtBf16> { bf16x8 a[2][4]; bf16x8 b[2][4]; };
+template <> struct StageFrags<kWtFp8> { i32x8 a[4]; i32x8 b[4]; };
+template <> struct StageFrags<kWtMxfp4> { i32x8 a[4]; u32x4 b[4]; };
 }  // namespace
 
 // Block work: one (256-row tile, column tile).  Wave (wm, wn) owns the 32-row MFMA
@@ -56,11 +79,14 @@ template <> struct StageFrags<true> { i32x8 a[4]; i32x8 b[4]; };
 // from registers while reading the fragments of stage j + 1 and loading stage j + 4
 // into the slot of stage j, whose fragments were read in the previous iteration.  So
 // three stages are in flight while one is computed.
-template <int MODE, bool GATHER, bool FP8>
+template <int MODE, bool GATHER, int WT>
 __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     constexpr int BM = kPrefillBM, BN = 256, MI = 4, NST = kStages;
-    constexpr int EB = FP8 ? 1 : 2;                     // bytes per element
+    constexpr bool Q8 = WT != kWtBf16;                  // E4M3 activations with row scales
+    constexpr int EB = Q8 ? 1 : 2;                      // bytes per activation element
     constexpr int BK = kStageRowBytes / EB;             // K per stage
+    constexpr int BRB = b_row_bytes<WT>();              // bytes per B row per stage
+    constexpr int SB = stage_bytes<WT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
     const int n_tiles_n = g.n_out / NCOL;
@@ -76,7 +102,8 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
-    const int64_t krow = static_cast<int64_t>(g.kd) * EB;     // bytes per weight row
+    // bytes per weight row (MXFP4: two values per byte)
+    const int64_t krow = (WT == kWtMxfp4) ? g.kd / 2 : static_cast<int64_t>(g.kd) * EB;
 
     // MFMA row tiles of this wave that hold rows of the expert (wave-uniform; a prefix of
     // the wave's tiles): the others skip their loads, LDS reads and MFMAs.
@@ -96,22 +123,26 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
         ag[i] = static_cast<const uint8_t*>(g.a) + arow * g.lda * EB + soff;
     }
-    // B rows of wave w are affine in j (for gate/up, waves 0-1 move gate rows, 2-3 up rows)
-    const uint8_t* bg;
-    {
-        const int r = wave * 64 + dr;
-        int64_t wrow;
-        if (MODE == kGateUp) wrow = (wave < 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
-        else wrow = c0 + r;
-        bg = static_cast<const uint8_t*>(g.w) + (static_cast<int64_t>(e) * nw + wrow) * krow + soff;
-    }
-    const int64_t bstep = 16 * krow;      // bytes between B rows j and j + 1
+    // B rows of wave w are affine in j (for gate/up, waves 0-1 move gate rows, 2-3 up rows).
+    // BF16 / FP8: rows w*64 + 16 j + lane/4, lane i fetching the chunk of LDS slot i % 4;
+    // MXFP4 (32-byte rows): rows w*64 + 32 j + lane/2, chunk of slot i % 2.
+    constexpr int BRPI = (WT == kWtMxfp4) ? 32 : 16;     // B rows per DMA instruction
+    constexpr int BJ = 64 / BRPI;                         // B DMA instructions per wave
+    const int bdr = (WT == kWtMxfp4) ? (lane >> 1) : dr;
+    const int bsoff = (WT == kWtMxfp4) ? (((lane & 1) ^ ((lane >> 4) & 1)) << 4) : soff;
+    auto weight_row = [&](int r) -> int64_t {            // block row r (0..255) -> weight row
+        if (MODE == kGateUp) return (r < BN / 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
+        return c0 + r;
+    };
+    const uint8_t* bg = static_cast<const uint8_t*>(g.w) +
+                        (static_cast<int64_t>(e) * nw + weight_row(wave * 64 + bdr)) * krow + bsoff;
+    const int64_t bstep = BRPI * krow;    // bytes between B rows j and j + 1
 
     // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l (gate-column
     // block in s_lo, up-column block in s_hi for gate/up; this wave's column block for
     // down).  kd / 128 <= 64 K blocks (hidden and inter are at most 8192).
     int s_lo = kUnitScale, s_hi = kUnitScale;
-    if constexpr (FP8) {
+    if constexpr (WT == kWtFp8) {
         const int kb_n = g.kd / 128;
         const float* r_lo;
         const float* r_hi;
@@ -126,6 +157,18 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         const int l = min(lane, kb_n - 1);
         s_lo = (__float_as_uint(r_lo[l]) >> 23) & 0xff;
         s_hi = (__float_as_uint(r_hi[l]) >> 23) & 0xff;
+    }
+    // MXFP4 block scales: the block's 256 weight rows x kd/32 E8M0 codes, staged in LDS
+    // after the stages (thread t copies row t; the rows of one half are contiguous).
+    const int srow = g.kd / 32;
+    uint8_t* ssc = smem + NST * SB;
+    if constexpr (WT == kWtMxfp4) {
+        const uint8_t* src = static_cast<const uint8_t*>(g.w_scale) +
+                             (static_cast<int64_t>(e) * nw + weight_row(tid)) * srow;
+        for (int c = 0; c < srow; c += 16)
+            *reinterpret_cast<u32x4*>(ssc + tid * srow + c) = *reinterpret_cast<const u32x4*>(src + c);
+        // complete before the pipeline: its waits count the direct-to-LDS loads alone
+        __syncthreads();
     }
 
     f32x16 acc[MI][4];
@@ -150,27 +193,28 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     // The K loop is instantiated per count MV of live row tiles, so no instance tests them.
     auto k_loop = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
-        constexpr int PER = MV + 4;                     // direct-to-LDS loads per stage and wave
-        constexpr int NM = (FP8 ? 4 : 8) * MV;          // MFMAs per stage
-        constexpr int NR = MV > 0 ? 2 * (MV + 4) : 0;   // 16-byte LDS reads per stage
+        constexpr int PER = MV + BJ;                    // direct-to-LDS loads per stage and wave
+        constexpr int NM = (WT == kWtBf16 ? 8 : 4) * MV;   // MFMAs per stage
+        constexpr int NR = MV == 0 ? 0 : (WT == kWtMxfp4 ? 2 * MV + 8 : 2 * (MV + 4));   // LDS reads
         auto dma = [&](int slot, int kt) {
-            uint8_t* As = smem + slot * kStageBytes;
+            uint8_t* As = smem + slot * SB;
             uint8_t* Bs = As + BM * kStageRowBytes;
             const int64_t kb = static_cast<int64_t>(kt) * kStageRowBytes;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
                 if (i < MV) lds_dma16(ag[i] + kb, As + ((wm + 2 * i) * 32 + 16 * wn) * kStageRowBytes);
+            const int64_t kbb = static_cast<int64_t>(kt) * BRB;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                lds_dma16(bg + j * bstep + kb, Bs + (wave * 64 + j * 16) * kStageRowBytes);
+            for (int j = 0; j < BJ; ++j)
+                lds_dma16(bg + j * bstep + kbb, Bs + (wave * 64 + j * BRPI) * BRB);
         };
         auto rd = [&](const uint8_t* T, int row, int c) {
             return *reinterpret_cast<const u32x4*>(T + stage_offset(row, c));
         };
-        auto load_frags = [&](StageFrags<FP8>& f, int slot) {
-            const uint8_t* As = smem + slot * kStageBytes;
+        auto load_frags = [&](StageFrags<WT>& f, int slot) {
+            const uint8_t* As = smem + slot * SB;
             const uint8_t* Bs = As + BM * kStageRowBytes;
-            if constexpr (FP8) {
+            if constexpr (WT == kWtFp8) {
                 // 32 bytes per lane: K values 32 lh .. 32 lh + 31 = chunks 2 lh, 2 lh + 1
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
@@ -179,6 +223,18 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni)
                         f.b[ni] = join8(rd(Bs, brow_l[ni], 2 * lh), rd(Bs, brow_l[ni], 2 * lh + 1));
+                }
+            } else if constexpr (WT == kWtMxfp4) {
+                // B lane: its column's MX block lh (K 32 lh .. 32 lh + 31, 16 bytes); the E4M3
+                // A lane that pairs with it holds K 16 lh .. +15 and 32 + 16 lh .. +15 (the
+                // operand layout of this MFMA with an FP4 B, measured on gfx950)
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    if (mi < MV) f.a[mi] = join8(rd(As, arow_l[mi], lh), rd(As, arow_l[mi], lh + 2));
+                if (MV > 0) {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        f.b[ni] = *reinterpret_cast<const u32x4*>(Bs + fp4_offset(brow_l[ni], lh));
                 }
             } else {
                 // K step ks: 16 bytes per lane, chunk 2 ks + lh
@@ -195,8 +251,8 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                 }
             }
         };
-        auto mfma_stage = [&](const StageFrags<FP8>& f, int kt) {
-            if constexpr (FP8) {
+        auto mfma_stage = [&](const StageFrags<WT>& f, int kt) {
+            if constexpr (WT == kWtFp8) {
                 const int kb = kt >> 1;                 // 128-wide K block of this stage
                 const int sc_lo = __builtin_amdgcn_readlane(s_lo, kb);
                 const int sc_hi = __builtin_amdgcn_readlane(s_hi, kb);
@@ -210,6 +266,20 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                                 f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0, kUnitScale, 0, sb);
                         }
                     }
+            } else if constexpr (WT == kWtMxfp4) {
+                if (MV > 0) {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        // E8M0 code of this lane's column, MX block 2 kt + lh
+                        const int sb = ssc[(brow_l[ni]) * srow + 2 * kt + lh];
+                        const i32x8 bb = fp4_operand(f.b[ni]);
+#pragma unroll
+                        for (int mi = 0; mi < MI; ++mi)
+                            if (mi < MV)
+                                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    f.a[mi], bb, acc[mi][ni], 0, 4, 0, kUnitScale, 0, sb);
+                    }
+                }
             } else {
                 (void)kt;
 #pragma unroll
@@ -225,7 +295,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
             }
         };
 
-        StageFrags<FP8> f0, f1;
+        StageFrags<WT> f0, f1;
 #pragma unroll
         for (int s = 0; s < NST; ++s) dma(s, min(s, nk - 1));
         wait_lds_dma<(NST - 1) * PER>();
@@ -236,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         // between them.  Unrolled by two so the fragment buffers alternate statically; the
         // body is branch-free: past the end the slab index is clamped and the last
         // iterations re-load the last slab into slots nothing reads any more.
-        auto iteration = [&](StageFrags<FP8>& cur, StageFrags<FP8>& nxt, int j, int slot) {
+        auto iteration = [&](StageFrags<WT>& cur, StageFrags<WT>& nxt, int j, int slot) {
             const int nslot = (slot + 1 == NST) ? 0 : slot + 1;
             __builtin_amdgcn_sched_barrier(0);
             wait_lds_dma<(NST - 2) * PER>();
@@ -265,7 +335,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
             const int m = (wm + 2 * mi) * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
             if (m >= rows) continue;
             float sa = 1.0f;
-            if constexpr (FP8) {
+            if constexpr (Q8) {
                 const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
                 sa = g.a_scale[ar];
             }
@@ -284,36 +354,38 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     }
 }
 
-template <int MODE, bool GATHER, bool FP8>
+template <int MODE, bool GATHER, int WT>
 static void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks) {
     static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, FP8>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes_max<WT>()));
         attr_set = true;
     }
-    gemm_prefill<MODE, GATHER, FP8><<<blocks, 256, kLdsBytes, st>>>(g);
+    const size_t lds = kStages * stage_bytes<WT>() + (WT == kWtMxfp4 ? 256 * static_cast<size_t>(g.kd / 32) : 0);
+    gemm_prefill<MODE, GATHER, WT><<<blocks, 256, lds, st>>>(g);
 }
 
-template <bool FP8>
+template <int WT>
 static void launch_prefill_dtype(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks) {
     if (mode == kGateUp) {
-        if (g.gather) launch_prefill_inst<kGateUp, true, FP8>(st, g, blocks);
-        else launch_prefill_inst<kGateUp, false, FP8>(st, g, blocks);
+        if (g.gather) launch_prefill_inst<kGateUp, true, WT>(st, g, blocks);
+        else launch_prefill_inst<kGateUp, false, WT>(st, g, blocks);
     } else {
-        if (g.gather) launch_prefill_inst<kDown, true, FP8>(st, g, blocks);
-        else launch_prefill_inst<kDown, false, FP8>(st, g, blocks);
+        if (g.gather) launch_prefill_inst<kDown, true, WT>(st, g, blocks);
+        else launch_prefill_inst<kDown, false, WT>(st, g, blocks);
     }
 }
 
-void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8) {
+void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt) {
     if (g.max_tiles == 0) return;
     const int ncol = (mode == kGateUp) ? 128 : 256;
     // every (row tile, column tile) of whole groups of group_m row tiles, in whole XCD chunks
     const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
     const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
-    if (fp8) launch_prefill_dtype<true>(st, mode, g, blocks);
-    else launch_prefill_dtype<false>(st, mode, g, blocks);
+    if (wt == PrefillWeights::kFp8) launch_prefill_dtype<kWtFp8>(st, mode, g, blocks);
+    else if (wt == PrefillWeights::kMxfp4) launch_prefill_dtype<kWtMxfp4>(st, mode, g, blocks);
+    else launch_prefill_dtype<kWtBf16>(st, mode, g, blocks);
 }
 
 }  // namespace beam

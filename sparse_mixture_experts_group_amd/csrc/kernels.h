@@ -92,8 +92,10 @@ void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArg
 void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 // gemm_mxfp4.hip: MXFP4 weights, E4M3 activations, weight streaming
 void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
-// gemm_prefill.hip: 256 x 256 LDS-tiled MFMA, BF16 or FP8 operands
-void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8);
+// gemm_prefill.hip: 256 x 256 LDS-tiled MFMA, BF16, FP8 or MXFP4 weights
+enum class PrefillWeights { kBf16, kFp8, kMxfp4 };
+constexpr int kMxfp4PrefillMaxKd = 8192;    // LDS holds a tile's weight scales
+void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
 
 // elementwise.hip
 void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,

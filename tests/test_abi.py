@@ -97,14 +97,16 @@ def test_argument_errors_before_any_launch():
     assert st == bm.BEAM_ERR_INVALID_ARG
 
 
-def test_mxfp4_needs_scales_and_the_streaming_range():
+def test_mxfp4_needs_scales_and_bounded_k_above_the_streaming_range():
     c = beam(weight_dtype=bm.BEAM_DTYPE_MXFP4)
     L = bm.lib()
     fwd = lambda T, s13, s2: L.beam_moe_forward(ctypes.byref(c), T, FAKE, FAKE, None, None, FAKE, s13, FAKE, s2,
                                                 FAKE, None, None, FAKE, 1 << 40, None)
     assert fwd(16, None, FAKE) == bm.BEAM_ERR_INVALID_ARG          # both scale arrays required
-    assert fwd(257, FAKE, FAKE) == bm.BEAM_ERR_UNSUPPORTED         # streaming kernels only
-    assert bm.beam_moe_workspace_size(c, 256) > 0
+    assert bm.beam_moe_workspace_size(c, 4096) > 0
+    # above the streaming range a tile's weight scales must fit in LDS (K <= 8192)
+    c = beam(weight_dtype=bm.BEAM_DTYPE_MXFP4, hidden=10240)
+    assert fwd(257, FAKE, FAKE) == bm.BEAM_ERR_UNSUPPORTED
 
 
 def test_route_and_sublayer_argument_errors():
