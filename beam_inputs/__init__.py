@@ -32,6 +32,8 @@ TAG_W13 = 3
 TAG_W2 = 4
 TAG_PERM = 5
 TAG_H = 6
+TAG_DW13 = 7      # dense MLP gate/up weights
+TAG_DW2 = 8       # dense MLP down weights
 
 DT_F32, DT_BF16, DT_FP8, DT_MXFP4 = 0, 1, 2, 3
 DTYPE_NAMES = {DT_F32: "f32", DT_BF16: "bf16", DT_FP8: "fp8_e4m3", DT_MXFP4: "mxfp4"}
@@ -189,6 +191,7 @@ class Workload:
     x_recipe: str = "normal"      # "normal" | "rms_normal"
     zipf_s: float | None = None    # skewed routing: per-expert logit offsets
     sublayer: bool = False         # pre-norm -> MoE -> post-norm -> residual
+    dense: bool = False            # dense SwiGLU MLP (one weight set, no router) in place of the MoE
     step_k: int = 10
     norm_eps: float = 1e-6
     fp8_block: int = 128
@@ -218,6 +221,12 @@ WORKLOADS = {
                                       weight_dtype=DT_MXFP4, x_recipe="rms_normal"),
     "beam_prefill_mxfp4_t4096": Workload("beam_prefill_mxfp4_t4096", T=4096, H=5120, I=2560, E=256, G=8, Kg=4,
                                          K=8, weight_dtype=DT_MXFP4),
+    # dense SwiGLU MLP of the first decoder layers, width 8 x 2560 = 20480 (the routed
+    # width of one MoE layer; the pages do not give the dense width)
+    "beam_dense_decode_t16": Workload("beam_dense_decode_t16", T=16, H=5120, I=20480, E=1, G=1, Kg=1, K=1,
+                                      alpha=1.0, dense=True, x_recipe="rms_normal"),
+    "beam_dense_prefill_t4096": Workload("beam_dense_prefill_t4096", T=4096, H=5120, I=20480, E=1, G=1, Kg=1,
+                                         K=1, alpha=1.0, dense=True),
 }
 
 
@@ -261,7 +270,7 @@ class Inputs:
     """Materialised inputs of one workload (host memory, storage formats)."""
     w: Workload
     x: np.ndarray                  # [T,H] float32 (F32 acts) or uint16 BF16 bits
-    w_router: np.ndarray           # [H,E] float32
+    w_router: np.ndarray | None    # [H,E] float32 (None for the dense MLP)
     logit_bias: np.ndarray | None  # [E] float32 or None
     w13: np.ndarray                # [E,2I,H] float32 | uint16 bf16 bits | uint8 e4m3
     w2: np.ndarray                 # [E,H,I]  same dtype family as w13
@@ -271,8 +280,9 @@ class Inputs:
 
 
 def _expert_draw(w: Workload, e: int):
-    g13 = normal(w.seed, (TAG_W13, e), (2 * w.I, w.H), std=1.0 / math.sqrt(w.H))
-    g2 = normal(w.seed, (TAG_W2, e), (w.H, w.I), std=1.0 / math.sqrt(w.I))
+    t13, t2 = (TAG_DW13, TAG_DW2) if w.dense else (TAG_W13, TAG_W2)
+    g13 = normal(w.seed, (t13, e), (2 * w.I, w.H), std=1.0 / math.sqrt(w.H))
+    g2 = normal(w.seed, (t2, e), (w.H, w.I), std=1.0 / math.sqrt(w.I))
     return g13, g2
 
 
@@ -287,7 +297,8 @@ def make_inputs(w: Workload, experts: list[int] | None = None) -> Inputs:
     x = token_inputs(w)
     if w.act_dtype == DT_BF16:
         x = to_bf16_bits(x)
-    w_router = normal(w.seed, (TAG_WROUTER,), (w.H, w.E), std=1.0 / math.sqrt(w.H))
+    # the dense MLP has no router: its single weight set is slot 0 of w13 / w2
+    w_router = None if w.dense else normal(w.seed, (TAG_WROUTER,), (w.H, w.E), std=1.0 / math.sqrt(w.H))
     bias = zipf_logit_offsets(w.E, w.zipf_s, w.seed) if w.zipf_s is not None else None
     E, I, H = w.E, w.I, w.H
     if w.weight_dtype == DT_F32:

@@ -17,6 +17,8 @@ constant scale"):
   combine  y = sum_i w_i o_i                                          float64
   sublayer h' = sqrt((k-1)/k) h + (1/sqrt k) RMSNorm(y),
            with the MoE input RMSNorm(h) (FP32, C)                    float64
+  dense    y = Wd (SiLU(Wg x) * (Wu x)), the MLP of the first 3 layers
+           (section "Architecture"), alone or inside the same sublayer float64
 
 The router and the pre-norm are FP32 because the pages fix those sites to FP32
 and their result decides integers (expert ids); every other step is float64, a
@@ -330,6 +332,37 @@ def sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, eps: flo
     Returns dict(ids, w, y (MoE output), h_new (float64), tokens)."""
     xhat, _ = prenorm(h32, pre_gain, eps)
     r = moe_forward(xhat, w_router, bias, bank, G, Kg, K, alpha, token_subset, select_bias)
+    tok = r["tokens"]
+    yn = rmsnorm64(r["y"], post_gain, eps)
+    r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)
+    r["xhat"] = xhat
+    return r
+
+
+# ---------------------------------------------------------------------------
+# dense SwiGLU MLP of the first decoder layers
+# ---------------------------------------------------------------------------
+def dense_forward(x32: np.ndarray, bank: ExpertBank, token_subset: np.ndarray | None = None):
+    """Dense SwiGLU MLP (Reflection Beam 1.0 overview, "Architecture": the first 3 of the
+    52 decoder layers run a dense SwiGLU MLP where the others run the MoE block):
+    y[t] = Wd (SiLU(Wg x_t) * (Wu x_t)) in float64, with the single weight set held in
+    slot 0 of `bank` (w13 [1, 2I, H], w2 [1, H, I], the layouts of one expert).  No
+    router and no combine weight.  The dense width I is not on the pages.
+    Returns dict(y [n,H] float64, tokens)."""
+    tok = np.arange(x32.shape[0]) if token_subset is None else np.asarray(token_subset)
+    w13, w2 = bank.expert(0)
+    y = expert_ffn(x32[tok].astype(np.float64), w13, w2)
+    return {"y": y, "tokens": tok}
+
+
+def dense_sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, eps: float,
+                           bank: ExpertBank, token_subset: np.ndarray | None = None):
+    """pre-RMSNorm (FP32, fixed order) -> dense SwiGLU MLP -> post-RMSNorm ->
+    constant-scale residual: the MoE sublayer with the dense MLP in the middle (the
+    pages normalise every sublayer before and after).
+    Returns dict(y (MLP output), h_new (float64), tokens, xhat)."""
+    xhat, _ = prenorm(h32, pre_gain, eps)
+    r = dense_forward(xhat, bank, token_subset)
     tok = r["tokens"]
     yn = rmsnorm64(r["y"], post_gain, eps)
     r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)

@@ -1,9 +1,10 @@
 """Checks of the seeded input generator (beam_inputs) against independent routines."""
+import math
 import numpy as np
 import torch
 
 import oracle
-from beam_inputs import (WORKLOADS, encode_e4m3, encode_e2m1, make_inputs, quantize_e4m3_blocks, quantize_mxfp4,
+from beam_inputs import (DT_F32, WORKLOADS, encode_e4m3, encode_e2m1, make_inputs, quantize_e4m3_blocks, quantize_mxfp4,
                          to_bf16_bits,
                          token_inputs, zipf_logit_offsets, normal)
 
@@ -107,3 +108,15 @@ def test_tiny_inputs_shapes():
     inp = make_inputs(WORKLOADS["tiny_f32"])
     assert inp.x.shape == (64, 128) and inp.x.dtype == np.float32
     assert inp.w13.shape == (16, 128, 128) and inp.w2.shape == (16, 128, 64)
+
+
+def test_dense_workload_draws_its_own_weights():
+    """The dense MLP has no router and one weight set, drawn from its own streams (not
+    expert 0's); the fan-in scaling is the experts' (1/sqrt(H), 1/sqrt(I))."""
+    from dataclasses import replace
+    d = replace(WORKLOADS["beam_dense_decode_t16"], H=256, I=512, T=4, weight_dtype=DT_F32, act_dtype=DT_F32)
+    inp = make_inputs(d)
+    assert inp.w_router is None and inp.w13.shape == (1, 1024, 256) and inp.w2.shape == (1, 256, 512)
+    moe = make_inputs(replace(d, dense=False, E=2, G=1, Kg=1, K=1), experts=[0])
+    assert not np.array_equal(inp.w13[0], moe.w13[0])
+    assert abs(inp.w13.std() * 16 - 1) < 0.02 and abs(inp.w2.std() * math.sqrt(512) - 1) < 0.02

@@ -400,6 +400,71 @@ def test_combine_linear_in_down_projection():
 
 
 # ---------------------------------------------------------------------------
+# dense SwiGLU MLP (first decoder layers)
+# ---------------------------------------------------------------------------
+def _one_slot(w13, w2):
+    return oracle.ExpertBank(w13[None].astype(np.float32), w2[None].astype(np.float32), "f32")
+
+
+def test_dense_impulse_closed_form_and_token_subset():
+    """Token 0 = c e_h0, token 1 = 0: y[0] = d SiLU(a c) (b c) e_m0 with a c = ln 3
+    (SiLU(ln 3) = 0.75 ln 3), y[1] = 0; a token subset returns just those rows."""
+    H, I = 10, 6
+    h0, j0, m0 = 4, 5, 9
+    c, a, b, dd = 3.0, math.log(3.0) / 3.0, 0.5, -2.0
+    x = np.zeros((2, H), np.float32); x[0, h0] = c
+    w13 = np.zeros((2 * I, H)); w13[j0, h0] = a; w13[I + j0, h0] = b
+    w2 = np.zeros((H, I)); w2[m0, j0] = dd
+    bank = oracle.ExpertBank(w13[None].astype(np.float64), w2[None].astype(np.float64), "f32")
+    bank.w13, bank.w2 = w13[None], w2[None]          # exact float64 values
+    r = oracle.dense_forward(x, bank)
+    expect = np.zeros((2, H)); expect[0, m0] = dd * 0.75 * math.log(3.0) * (b * c)
+    assert np.allclose(r["y"], expect, rtol=1e-14, atol=1e-15)
+    r1 = oracle.dense_forward(x, bank, token_subset=np.array([1]))
+    assert r1["y"].shape == (1, H) and np.all(r1["y"] == 0.0) and list(r1["tokens"]) == [1]
+
+
+def test_dense_is_the_moe_with_identical_experts_over_alpha():
+    """A MoE layer whose experts all hold the dense weights returns alpha * dense(x)
+    whatever the routing (the combine weights sum to alpha)."""
+    w = WORKLOADS["tiny_f32"]
+    rs = np.random.default_rng(5)
+    bank = _tiny_bank(rs, w.E, w.H, w.I, same=True)
+    x = rs.standard_normal((24, w.H)).astype(np.float32)
+    wr = rs.standard_normal((w.H, w.E)).astype(np.float32)
+    moe = oracle.moe_forward(x, wr, None, bank, w.G, w.Kg, w.K, w.alpha)
+    dense = oracle.dense_forward(x, oracle.ExpertBank(bank.w13[:1], bank.w2[:1], "f32"))
+    assert np.allclose(moe["y"], w.alpha * dense["y"], rtol=1e-6, atol=1e-6)
+
+
+def test_dense_sublayer_zero_down_projection_keeps_the_scaled_stream():
+    """Wd = 0 gives y = 0, RMSNorm(0) = 0, so h' = sqrt((k-1)/k) h exactly."""
+    rs = np.random.default_rng(6)
+    H, I, k = 64, 32, 7
+    h = rs.standard_normal((5, H)).astype(np.float32)
+    bank = _one_slot(rs.standard_normal((2 * I, H)), np.zeros((H, I)))
+    r = oracle.dense_sublayer_forward(h, None, None, k, 1e-6, bank)
+    assert np.all(r["y"] == 0.0)
+    assert np.array_equal(r["h_new"], math.sqrt((k - 1) / k) * h.astype(np.float64))
+
+
+def test_dense_sublayer_matches_moe_sublayer_with_identical_experts():
+    """With alpha = 1 and every expert holding the dense weights, the MoE sublayer and
+    the dense sublayer compute the same h' (up to the FP32 combine weights)."""
+    w = WORKLOADS["tiny_f32"]
+    rs = np.random.default_rng(7)
+    bank = _tiny_bank(rs, w.E, w.H, w.I, same=True)
+    h = rs.standard_normal((12, w.H)).astype(np.float32)
+    wr = rs.standard_normal((w.H, w.E)).astype(np.float32)
+    g1 = (1 + 0.1 * rs.standard_normal(w.H)).astype(np.float32)
+    g2 = (1 + 0.1 * rs.standard_normal(w.H)).astype(np.float32)
+    moe = oracle.sublayer_forward(h, g1, g2, 5, 1e-6, wr, None, bank, w.G, w.Kg, w.K, 1.0)
+    dense = oracle.dense_sublayer_forward(h, g1, g2, 5, 1e-6,
+                                          oracle.ExpertBank(bank.w13[:1], bank.w2[:1], "f32"))
+    assert np.allclose(moe["h_new"], dense["h_new"], rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
 # storage formats
 # ---------------------------------------------------------------------------
 def test_e4m3_decode_matches_spec_facts_and_torch():
