@@ -4,9 +4,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 python bench.py --workload NAME --sweep 16,64,256,... [--steps K]   (one line per T)
 
 A step is one full `beam_moe_forward` (router, permutation, gate/up GEMM with SwiGLU,
-down GEMM, combine) -- or `beam_moe_sublayer_forward` for the sublayer workload -- over
-one batch of seeded synthetic Beam-shaped inputs already resident in HBM.  Prints ONE
-JSON line on stdout; progress goes to stderr.
+down GEMM, combine) -- or `beam_moe_sublayer_forward` for the sublayer workload, and
+`beam_dense_forward` for the dense-MLP workloads -- over one batch of seeded synthetic
+Beam-shaped inputs already resident in HBM.  Prints ONE JSON line on stdout; progress
+goes to stderr.
 
 Default workload: the Beam-shaped decode batch (T = 16 tokens, hidden 5120, 256 experts
 in 8 groups of 32, top-4 groups, top-8, SwiGLU intermediate 2560, BF16 experts), where
@@ -85,14 +86,18 @@ class Layer:
             return torch.from_numpy(a).to(dev)
 
         self.x_all = up(inp.x)
-        self.wr = up(inp.w_router)
+        self.wr = up(inp.w_router) if inp.w_router is not None else None
         self.w13, self.w2 = up(inp.w13), up(inp.w2)
         self.s13 = up(inp.w13_scale) if inp.w13_scale is not None else None
         self.s2 = up(inp.w2_scale) if inp.w2_scale is not None else None
         self.bias = up(inp.logit_bias) if inp.logit_bias is not None else None
-        self.cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg,
-                                  topk=w.K, routed_scale=w.alpha, act_dtype=w.act_dtype,
-                                  weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+        if w.dense:
+            self.cfg = bm.make_dense_config(hidden=w.H, inter=w.I, act_dtype=w.act_dtype,
+                                            weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+        else:
+            self.cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg,
+                                      topk=w.K, routed_scale=w.alpha, act_dtype=w.act_dtype,
+                                      weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
 
     def measure(self, T: int, steps: int, warmup: int) -> dict:
         """Time `steps` forwards over the first T tokens (after `warmup` untimed ones):
@@ -101,14 +106,20 @@ class Layer:
         import torch
         bm, w = self.bm, self.w
         x = self.x_all[:T].contiguous()
-        ws = bm.alloc_workspace(self.cfg, T, self.dev)
+        ws = (bm.alloc_dense_workspace if w.dense else bm.alloc_workspace)(self.cfg, T, self.dev)
         ids = torch.empty((T, w.K), dtype=torch.int32, device=self.dev)
         wts = torch.empty((T, w.K), dtype=torch.float32, device=self.dev)
         y = torch.empty_like(x)
         h = x.clone()      # the sublayer updates the residual stream in place, step after step
 
         def step():
-            if w.sublayer:
+            if w.dense and w.sublayer:
+                bm.beam_dense_sublayer_forward(self.cfg, h, w.step_k, self.w13, self.w2, w13_scale=self.s13,
+                                               w2_scale=self.s2, ws=ws)
+            elif w.dense:
+                bm.beam_dense_forward(self.cfg, x, self.w13, self.w2, w13_scale=self.s13, w2_scale=self.s2, y=y,
+                                      ws=ws)
+            elif w.sublayer:
                 bm.beam_moe_sublayer_forward(self.cfg, h, w.step_k, self.wr, self.w13, self.w2,
                                              logit_bias=self.bias, w13_scale=self.s13, w2_scale=self.s2,
                                              ids=ids, weights=wts, ws=ws)
@@ -134,8 +145,11 @@ class Layer:
         ms_wall = (wall1 - wall0) * 1e3 / steps
         kernel_ms = {"gate_up": round(float(np.mean(timer.times_ms())), 4)}
         # per-kernel times (separate passes after the timed region)
-        for name, kid in (("router_logits", bm.BEAM_KERNEL_ROUTER_LOGITS), ("down", bm.BEAM_KERNEL_DOWN),
-                          ("combine", bm.BEAM_KERNEL_COMBINE)):
+        others = [("router_logits", bm.BEAM_KERNEL_ROUTER_LOGITS), ("down", bm.BEAM_KERNEL_DOWN),
+                  ("combine", bm.BEAM_KERNEL_COMBINE)]
+        if w.dense:             # no router; the combine kernel only inside the sublayer
+            others = [o for o in others if o[0] == "down" or (o[0] == "combine" and w.sublayer)]
+        for name, kid in others:
             n = min(steps, 3)
             kt = bm.KernelTimer(kid, n)
             with kt:
@@ -143,6 +157,9 @@ class Layer:
                     step()
                 torch.cuda.synchronize()
             kernel_ms[name] = round(float(np.mean(kt.times_ms())), 4)
+        if w.dense:
+            return {"ms_gpu": ms_gpu, "ms_wall": ms_wall, "ms_per_step": max(ms_gpu, ms_wall),
+                    "kernel_ms": kernel_ms, "n_active": 1, "max_rows": T}
         ids_np = ids.cpu().numpy()
         return {"ms_gpu": ms_gpu, "ms_wall": ms_wall, "ms_per_step": max(ms_gpu, ms_wall),
                 "kernel_ms": kernel_ms, "n_active": int(np.unique(ids_np).size),
@@ -228,7 +245,7 @@ def main():
     # ---- whole-layer figures ----
     P = w.T * w.K
     wbytes = {0: 4, 1: 2, 2: 1, 3: 0.5}[w.weight_dtype]
-    layer_flops = 2.0 * P * w.H * 3 * w.I + 2.0 * w.T * w.H * w.E
+    layer_flops = 2.0 * P * w.H * 3 * w.I + (0.0 if w.dense else 2.0 * w.T * w.H * w.E)
     layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
     extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
              "layer_weight_gbs": round(layer_wbytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -248,7 +265,7 @@ def main():
         "data": "synthetic (seeded Philox normals, Beam-shaped, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
                    "groups": w.G, "topk_groups": w.Kg, "topk": w.K, "routed_scale": w.alpha,
-                   "weights": DTYPE_NAMES[w.weight_dtype], "sublayer": w.sublayer,
+                   "weights": DTYPE_NAMES[w.weight_dtype], "sublayer": w.sublayer, "dense_mlp": w.dense,
                    "zipf_s": w.zipf_s, "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu, "extra": extra,
     }
@@ -291,16 +308,23 @@ def cpu_baseline(w, inp, n_tok):
                              inp.w13_scale, inp.w2_scale, w.fp8_block)
     log(f"[bench] timing the CPU oracle on {n} tokens ...")
     t0 = time.perf_counter()
-    if w.sublayer:
+    if w.dense:
+        what = "float64 dense SwiGLU MLP"
+        if w.sublayer:
+            oracle.dense_sublayer_forward(x32, None, None, w.step_k, w.norm_eps, bank)
+        else:
+            oracle.dense_forward(x32, bank)
+    elif w.sublayer:
         oracle.sublayer_forward(x32, None, None, w.step_k, w.norm_eps, inp.w_router, inp.logit_bias, bank,
                                 w.G, w.Kg, w.K, w.alpha)
     else:
         oracle.moe_forward(x32, inp.w_router, inp.logit_bias, bank, w.G, w.Kg, w.K, w.alpha)
     dt = time.perf_counter() - t0
     log(f"[bench] CPU oracle: {dt:.2f}s")
+    if not w.dense:
+        what = "FP32 routing + float64 expert MLPs and combine"
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(max(oracle.num_threads(), blas)),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {n} tokens of {w.name}: FP32 routing + float64 expert MLPs and combine"}
+            "kind": "oracle", "seconds": round(dt, 2), "sample": f"first {n} tokens of {w.name}: {what}"}
 
 
 if __name__ == "__main__":

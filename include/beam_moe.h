@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BEAM_MOE_ABI_VERSION 2
+#define BEAM_MOE_ABI_VERSION 3
 
 typedef enum {
     BEAM_OK = 0,
@@ -62,7 +62,7 @@ typedef enum {
     BEAM_DTYPE_BF16 = 1,
     BEAM_DTYPE_FP8_E4M3 = 2,    /* OCP E4M3FN, block-scaled (power-of-two FP32 scales) */
     BEAM_DTYPE_MXFP4 = 3        /* OCP MX FP4 (E2M1 elements, E8M0 scale per 32 along K);
-                                   weights only, up to 256 tokens per call */
+                                   weights only */
 } beam_dtype;
 
 /*
@@ -71,11 +71,13 @@ typedef enum {
  *   group size S = n_experts / n_groups is >= 2; 1 <= topk_groups <= n_groups;
  *   1 <= topk <= min(32, topk_groups * S); routed_scale finite.
  * Kernel support (else BEAM_ERR_UNSUPPORTED):
- *   (act, weight) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)};
- *   hidden <= 16384; hidden and inter multiples of 64 for F32 weights and of 128
- *   otherwise (fp8_block must be 128);
+ *   (act, weight) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (BF16, MXFP4)};
+ *   hidden <= 16384; hidden and inter multiples of 64 for F32 weights; otherwise
+ *   hidden a multiple of 256 and inter of 128 (fp8_block must be 128);
  *   with V = ceil(n_experts / 64) scores per lane (V in {1, 2, 4}), S % V == 0 and
  *   S / V a power of two.
+ *   Above 256 tokens per call: hidden and inter <= 8192 for MXFP4 weights and
+ *   <= 32768 for FP8 weights (checked per call).
  * Beam: {5120, 2560, 256, 8, 4, 8, 2.5f, BF16, BF16 or FP8_E4M3, 128, 1e-6f}.
  */
 typedef struct beam_moe_config {
@@ -147,8 +149,7 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  *   y          device [T, H] act_dtype out
  *   ids_out    device [T, K] int32 out, or NULL;  weights_out device [T, K] FP32 or NULL
  * With FP8 or MXFP4 weights the activations entering each GEMM are quantised on the GPU
- * to E4M3 with one FP32 scale per row (the row's amax / 448).  MXFP4 weights are
- * supported up to 256 tokens per call (BEAM_ERR_UNSUPPORTED above).
+ * to E4M3 with one FP32 scale per row (the row's amax / 448).
  */
 int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x,
                      const float* w_router, const float* logit_bias,
@@ -200,6 +201,51 @@ typedef struct beam_moe_ws_map {
 } beam_moe_ws_map;
 
 int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_map* out);
+
+/*
+ * Dense SwiGLU MLP (Beam overview, section "Architecture": the first 3 of the 52
+ * decoder layers run a dense SwiGLU MLP where the other 49 run the MoE block; the pages
+ * do not give its intermediate size):
+ *   y[t] = Wd (SiLU(Wg x_t) * (Wu x_t))
+ * Of cfg only hidden (H), inter (the dense intermediate size I), act_dtype,
+ * weight_dtype, fp8_block and norm_eps are read (hidden, inter >= 1, dtypes in range,
+ * norm_eps finite and >= 0, else BEAM_ERR_INVALID_ARG); the router fields are ignored.
+ * Kernel support is that of the MoE layer's expert GEMMs (dtype pairs, multiples and
+ * per-call limits above), except that the streaming kernels, which read the weights
+ * once per 32 rows, serve up to 32 tokens and the LDS-tiled kernels above, and that
+ * above 32 tokens MXFP4 weights need hidden <= 8192 and inter a multiple of 512 s, s
+ * the least power of two with inter / s <= 8192 (s <= 16).  While the tiles are few
+ * both GEMMs split the reduction into slices whose FP32 partial sums the workspace
+ * holds.  The weights have the layout of one expert of beam_moe_forward (E = 1):
+ *   x          device [T, H] act_dtype
+ *   w13        device [2I, H] weight_dtype (rows 0..I-1 gate, I..2I-1 up; MXFP4
+ *              [2I, H/2] bytes);  w13_scale FP8 [2I/128, H/128] FP32 powers of two,
+ *              MXFP4 [2I, H/32] E8M0 codes, NULL otherwise
+ *   w2         device [H, I] weight_dtype (MXFP4 [H, I/2]);  w2_scale FP8
+ *              [H/128, I/128], MXFP4 [H, I/32], NULL otherwise
+ *   y          device [T, H] act_dtype out
+ *   ws         device workspace of ws_bytes >= beam_dense_workspace_size(cfg, T)
+ * The GEMMs and the E4M3 activation quantisation are those of beam_moe_forward.
+ */
+size_t beam_dense_workspace_size(const beam_moe_config* cfg, int64_t T);
+
+int beam_dense_forward(const beam_moe_config* cfg, int64_t T, const void* x, const void* w13,
+                       const void* w13_scale, const void* w2, const void* w2_scale, void* y,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense MLP sublayer with the constant-scale residual (as beam_moe_sublayer_forward
+ * with the dense MLP in place of the MoE block):
+ *   h <- c1 * h + c2 * RMSNorm(Dense(RMSNorm(h) * pre_gain)) * post_gain
+ *   h          device [T, H] BF16, updated in place (act_dtype must be BF16)
+ *   mlp_out    device [T, H] BF16 out (the MLP output before the post-norm), or NULL
+ *   other arguments as in beam_moe_sublayer_forward and beam_dense_forward.
+ */
+int beam_dense_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
+                                const float* pre_gain, const float* post_gain, int32_t step_k,
+                                const void* w13, const void* w13_scale, const void* w2,
+                                const void* w2_scale, void* mlp_out, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * Kernel timing hook (instrumentation for benchmarks; not needed for computing).

@@ -19,7 +19,8 @@ BEAM_DTYPE_F32, BEAM_DTYPE_BF16, BEAM_DTYPE_FP8_E4M3, BEAM_DTYPE_MXFP4 = range(4
 
 C_FUNCTIONS = ("beam_moe_status_string", "beam_moe_abi_version", "beam_moe_workspace_size",
                "beam_moe_workspace_map", "beam_moe_route", "beam_moe_forward",
-               "beam_moe_sublayer_forward", "beam_moe_time_kernel")
+               "beam_moe_sublayer_forward", "beam_moe_time_kernel", "beam_dense_workspace_size",
+               "beam_dense_forward", "beam_dense_sublayer_forward")
 BEAM_KERNEL_NONE, BEAM_KERNEL_ROUTER_LOGITS, BEAM_KERNEL_GATE_UP, BEAM_KERNEL_DOWN, BEAM_KERNEL_COMBINE = range(5)
 
 
@@ -82,6 +83,13 @@ def lib() -> ctypes.CDLL:
                                             vp, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_time_kernel.restype = ctypes.c_int
     L.beam_moe_time_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.beam_dense_workspace_size.restype = sz
+    L.beam_dense_workspace_size.argtypes = [cfgp, i64]
+    L.beam_dense_forward.restype = ctypes.c_int
+    L.beam_dense_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_dense_sublayer_forward.restype = ctypes.c_int
+    L.beam_dense_sublayer_forward.argtypes = [cfgp, i64, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz,
+                                              vp]
     _lib = L
     return L
 
@@ -207,4 +215,55 @@ def beam_moe_sublayer_forward(cfg, h, step_k, w_router, w13, w2, pre_gain=None, 
                                          _ptr(weights), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(stream))
     _check(st, "beam_moe_sublayer_forward")
+    return h
+
+
+# ---------------------------------------------------------------------------
+# dense SwiGLU MLP (the first decoder layers)
+# ---------------------------------------------------------------------------
+def make_dense_config(hidden=5120, inter=20480, act_dtype=BEAM_DTYPE_BF16, weight_dtype=BEAM_DTYPE_BF16,
+                      fp8_block=128, norm_eps=1e-6) -> beam_moe_config:
+    """Configuration of the dense MLP (only these fields are read; the router fields are
+    left at their defaults).  The default width 20480 is a reading (8 x 2560), not a
+    number on the pages."""
+    return make_config(hidden=hidden, inter=inter, act_dtype=act_dtype, weight_dtype=weight_dtype,
+                       fp8_block=fp8_block, norm_eps=norm_eps)
+
+
+def beam_dense_workspace_size(cfg: beam_moe_config, T: int) -> int:
+    return int(lib().beam_dense_workspace_size(ctypes.byref(cfg), int(T)))
+
+
+def alloc_dense_workspace(cfg: beam_moe_config, T: int, device="cuda"):
+    """Device workspace (uint8 tensor) sized by beam_dense_workspace_size."""
+    import torch
+    n = beam_dense_workspace_size(cfg, T)
+    if n == 0 and T > 0:
+        raise BeamMoEError(BEAM_ERR_INVALID_ARG, "beam_dense_workspace_size")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def beam_dense_forward(cfg, x, w13, w2, w13_scale=None, w2_scale=None, y=None, ws=None, stream=None):
+    """Dense SwiGLU MLP: returns y [T,H] (same dtype as x) on the GPU."""
+    import torch
+    T = x.shape[0]
+    y = torch.empty_like(x) if y is None else y
+    ws = alloc_dense_workspace(cfg, T, x.device) if ws is None else ws
+    st = lib().beam_dense_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                  _ptr(w2_scale), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(st, "beam_dense_forward")
+    return y
+
+
+def beam_dense_sublayer_forward(cfg, h, step_k, w13, w2, pre_gain=None, post_gain=None, w13_scale=None,
+                                w2_scale=None, mlp_out=None, ws=None, stream=None):
+    """pre-RMSNorm -> dense MLP -> post-RMSNorm -> constant-scale residual, updating h in place."""
+    T = h.shape[0]
+    ws = alloc_dense_workspace(cfg, T, h.device) if ws is None else ws
+    st = lib().beam_dense_sublayer_forward(ctypes.byref(cfg), T, _ptr(h), _ptr(pre_gain), _ptr(post_gain),
+                                           int(step_k), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                           _ptr(mlp_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream))
+    _check(st, "beam_dense_sublayer_forward")
     return h

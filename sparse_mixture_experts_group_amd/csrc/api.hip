@@ -1,6 +1,7 @@
 // C ABI of libbeam_moe: validation, workspace layout and kernel sequencing.
 // The declarations and the full contract of every entry point are in beam_moe.h.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "beam_moe.h"
@@ -35,21 +36,30 @@ bool config_valid(const beam_moe_config* c) {
     return true;
 }
 
-// Whether kernels exist for this (valid) configuration.
-bool config_supported(const beam_moe_config* c) {
+// Whether the expert GEMM kernels cover these dtypes and shapes (shared by the MoE layer
+// and the dense MLP).
+bool gemm_supported(const beam_moe_config* c) {
     const int a = c->act_dtype, w = c->weight_dtype;
     const bool pair_ok = (a == BEAM_DTYPE_F32 && w == BEAM_DTYPE_F32) ||
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_BF16) ||
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_FP8_E4M3) ||
                          (a == BEAM_DTYPE_BF16 && w == BEAM_DTYPE_MXFP4);
     if (!pair_ok) return false;
-    if (c->hidden > 16384) return false;   // LDS staging of the small-batch router kernel
+    // LDS staging of the small-batch router and of the norms: at most 16384 columns
+    if (c->hidden > 16384) return false;
     if (w == BEAM_DTYPE_F32) {
         if (c->hidden % 64 || c->inter % 64) return false;
     } else {
-        if (c->hidden % 128 || c->inter % 128) return false;
+        // the prefill down GEMM covers the hidden dimension in 256-column tiles
+        if (c->hidden % 256 || c->inter % 128) return false;
     }
     if (w == BEAM_DTYPE_FP8_E4M3 && c->fp8_block != 128) return false;
+    return true;
+}
+
+// Whether kernels exist for this (valid) configuration.
+bool config_supported(const beam_moe_config* c) {
+    if (!gemm_supported(c)) return false;
     const int V = scores_per_lane(c->n_experts);
     const int S = c->n_experts / c->n_groups;
     if (S % V != 0 || !is_pow2(S / V)) return false;
@@ -59,12 +69,33 @@ bool config_supported(const beam_moe_config* c) {
 
 struct Layout {
     size_t z, zpart, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
-    size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm;
+    size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm, part;
     size_t total;
     int nblk, max_tiles, bm;
 };
 
-Layout make_layout(const beam_moe_config& c, int64_t T) {
+// Slices the dense MLP's MXFP4 down GEMM needs above the streaming range, where a
+// slice's weight scales are staged in LDS (power of two).
+int dense_mxfp4_min_slices(const beam_moe_config& c) {
+    int s = 1;
+    while (c.inter / s > kMxfp4PrefillMaxKd) s *= 2;
+    return s;
+}
+
+// FP32 split-K partial sums of the dense MLP's GEMMs: half its gate/up weight bytes, or
+// four [T, H] slices (the down GEMM of a long prefill), whichever is larger.  The
+// launchers split while the grid holds fewer than four tiles per CU and the slices fit.
+int64_t dense_part_floats(const beam_moe_config& c, int64_t T) {
+    const double wb = c.weight_dtype == BEAM_DTYPE_BF16 ? 2.0 : (c.weight_dtype == BEAM_DTYPE_FP8_E4M3 ? 1.0 : 0.5);
+    int64_t f = static_cast<int64_t>(2.0 * c.inter * c.hidden * wb / 2.0 / sizeof(float));
+    f = std::max(f, 4 * T * c.hidden);
+    if (c.weight_dtype == BEAM_DTYPE_MXFP4) f = std::max(f, dense_mxfp4_min_slices(c) * T * c.hidden);
+    return (f + 63) / 64 * 64;
+}
+
+// Workspace regions.  dense: the dense MLP (c has n_experts = topk = 1): no router
+// regions, and FP32 split-K partial sums for its streaming down GEMM.
+Layout make_layout(const beam_moe_config& c, int64_t T, bool dense = false) {
     Layout L;
     const int64_t E = c.n_experts, K = c.topk, H = c.hidden, I = c.inter;
     const int64_t P = T * K;
@@ -77,14 +108,15 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     L.max_tiles = static_cast<int>((P + L.bm - 1) / L.bm + E);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
-    L.z = take(sizeof(float) * T * E);
+    L.z = take(dense ? 0 : sizeof(float) * T * E);
     // chunk sums of the small-T router kernel (only used below the tiled kernel's range)
-    L.zpart = take(router_uses_partials(T, static_cast<int>(H), static_cast<int>(E)) ? sizeof(float) * 64 * T * E : 0);
+    L.zpart = take((!dense && router_uses_partials(T, static_cast<int>(H), static_cast<int>(E)))
+                       ? sizeof(float) * 64 * T * E : 0);
     L.ids = take(sizeof(int32_t) * P);
     L.wts = take(sizeof(float) * P);
-    L.blk_cnt = take(sizeof(int32_t) * L.nblk * E);
-    L.blk_off = take(sizeof(int32_t) * L.nblk * E);
-    L.pair_rank = take(sizeof(int32_t) * P);
+    L.blk_cnt = take(dense ? 0 : sizeof(int32_t) * L.nblk * E);
+    L.blk_off = take(dense ? 0 : sizeof(int32_t) * L.nblk * E);
+    L.pair_rank = take(dense ? 0 : sizeof(int32_t) * P);
     L.exp_cnt = take(sizeof(int32_t) * E);
     L.exp_off = take(sizeof(int32_t) * (E + 1));
     L.tiles = take(sizeof(int2) * L.max_tiles);
@@ -94,7 +126,7 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     L.pair_of_row = take(sizeof(int32_t) * P);
     // sublayer (BF16 residual stream): FP32 normalised input for the router, and the
     // expert input in the weights' format
-    L.xhat32 = bf16_act ? take(sizeof(float) * T * H) : off;
+    L.xhat32 = (bf16_act && !dense) ? take(sizeof(float) * T * H) : off;
     L.x16 = (bf16_act && !fp8) ? take(sizeof(uint16_t) * T * H) : off;
     L.x8 = fp8 ? take(T * H) : off;
     L.x8s = fp8 ? take(sizeof(float) * T) : off;
@@ -102,6 +134,8 @@ Layout make_layout(const beam_moe_config& c, int64_t T) {
     L.h8 = fp8 ? take(P * I) : off;
     L.h8s = fp8 ? take(sizeof(float) * P) : off;
     L.yperm = take((f32 ? 4 : 2) * P * H);
+    // split-K partial sums of the dense MLP
+    L.part = take((dense && !f32) ? dense_part_floats(c, T) * sizeof(float) : 0);
     L.total = off;
     return L;
 }
@@ -204,22 +238,40 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     return g;
 }
 
-// Expert GEMMs: x_exp [T, H] in the weights' activation format -> yperm [T*K, H].
+// Expert GEMMs: x_exp [T, H] in the weights' activation format -> down_out [T*K, H]
+// (yperm for the MoE layer).  dense: the single weight set of the dense MLP (rows are
+// tokens, no gather), whose streaming down GEMM may split K into FP32 partial sums that
+// one more kernel adds up.
 void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
                  const void* x_exp, const float* x_exp_scale, const void* w13,
                  const void* w13_scale, const void* w2, const void* w2_scale,
-                 const int32_t* ids) {
+                 const int32_t* ids, void* down_out, bool dense = false) {
     const int64_t P = T * c.topk;
     const int H = c.hidden, I = c.inter;
     GroupedGemmArgs g1 = base_args(c, T, L, ws);
-    g1.a = x_exp; g1.lda = H; g1.gather = true; g1.a_scale = x_exp_scale;
+    g1.a = x_exp; g1.lda = H; g1.gather = !dense; g1.a_scale = x_exp_scale;
     g1.w = w13; g1.w_scale = w13_scale; g1.n_out = I; g1.kd = H;
     g1.out = at<void>(ws, L.hbuf); g1.ldo = I;
     GroupedGemmArgs g2 = base_args(c, T, L, ws);
     g2.lda = I; g2.gather = false;
     g2.w = w2; g2.w_scale = w2_scale; g2.n_out = H; g2.kd = I;
-    g2.out = at<void>(ws, L.yperm); g2.ldo = H;
-    const bool decode = T <= kDecodeMaxT;
+    g2.out = down_out; g2.ldo = H;
+    // streaming kernels while the rows of an expert are few: T tokens spread over the
+    // experts, or at most 32 rows of the dense MLP's single weight set (the streaming
+    // kernels read the weights once per 32 rows)
+    const bool decode = dense ? T <= kDenseStreamMaxT : T <= kDecodeMaxT;
+    if (dense && c.weight_dtype != BEAM_DTYPE_F32) {
+        g1.part = g2.part = at<float>(ws, L.part);
+        g1.part_cap = g2.part_cap = dense_part_floats(c, T);
+        g1.part_slice = P * 2 * I;
+        g2.part_slice = P * H;
+    }
+    int slices = 1, slices1 = 1;
+    // after a split gate/up GEMM: the SwiGLU of the summed partials into hbuf
+    auto swiglu = [&]() {
+        if (slices1 > 1)
+            launch_splitk_swiglu(st, slices1, P, I, g1.part_slice, g1.part, at<uint16_t>(ws, L.hbuf));
+    };
     if (c.weight_dtype == BEAM_DTYPE_F32) {
         { Bracket b(BEAM_KERNEL_GATE_UP, st); launch_gemm_f32(st, kGateUp, g1, P, ids); }
         g2.a = at<void>(ws, L.hbuf);
@@ -227,42 +279,46 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
     } else if (c.weight_dtype == BEAM_DTYPE_BF16) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) launch_gemm_bf16_decode(st, kGateUp, g1);
-            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kBf16);
+            if (decode) slices1 = launch_gemm_bf16_decode(st, kGateUp, g1);
+            else slices1 = launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kBf16);
         }
+        swiglu();
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) launch_gemm_bf16_decode(st, kDown, g2);
-            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kBf16);
+            if (decode) slices = launch_gemm_bf16_decode(st, kDown, g2);
+            else slices = launch_gemm_prefill(st, kDown, g2, PrefillWeights::kBf16);
         }
     } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) launch_gemm_fp8_decode(st, kGateUp, g1);
-            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kFp8);
+            if (decode) slices1 = launch_gemm_fp8_decode(st, kGateUp, g1);
+            else slices1 = launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kFp8);
         }
+        swiglu();
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) launch_gemm_fp8_decode(st, kDown, g2);
-            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kFp8);
+            if (decode) slices = launch_gemm_fp8_decode(st, kDown, g2);
+            else slices = launch_gemm_prefill(st, kDown, g2, PrefillWeights::kFp8);
         }
     } else {            // MXFP4 weights
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) launch_gemm_mxfp4_decode(st, kGateUp, g1);
-            else launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kMxfp4);
+            if (decode) slices1 = launch_gemm_mxfp4_decode(st, kGateUp, g1);
+            else slices1 = launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kMxfp4);
         }
+        swiglu();
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) launch_gemm_mxfp4_decode(st, kDown, g2);
-            else launch_gemm_prefill(st, kDown, g2, PrefillWeights::kMxfp4);
+            if (decode) slices = launch_gemm_mxfp4_decode(st, kDown, g2);
+            else slices = launch_gemm_prefill(st, kDown, g2, PrefillWeights::kMxfp4);
         }
     }
+    if (slices > 1) launch_splitk_reduce(st, slices, P * H, g2.part_slice, g2.part, static_cast<uint16_t*>(down_out));
 }
 
 }  // namespace
@@ -320,15 +376,27 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x, const f
 }
 
 static int check_weights(const beam_moe_config* cfg, int64_t T, const void* w13, const void* w13_scale,
-                         const void* w2, const void* w2_scale) {
+                         const void* w2, const void* w2_scale, bool dense = false) {
     if (!w13 || !w2) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(w13) || !aligned16(w2)) return BEAM_ERR_INVALID_ARG;
     const bool scaled = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4;
     if (scaled != (w13_scale != nullptr) || scaled != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
     if (scaled && (!aligned16(w13_scale) || !aligned16(w2_scale))) return BEAM_ERR_INVALID_ARG;
-    // above the streaming range, MXFP4 tiles stage their weight scales in LDS
-    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > kDecodeMaxT &&
-        (cfg->hidden > kMxfp4PrefillMaxKd || cfg->inter > kMxfp4PrefillMaxKd))
+    const int64_t stream_max = dense ? kDenseStreamMaxT : kDecodeMaxT;
+    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > stream_max) {
+        // above the streaming range, MXFP4 tiles stage their weight scales in LDS; the
+        // dense MLP's down GEMM splits K into slices whose scales fit
+        if (cfg->hidden > kMxfp4PrefillMaxKd) return BEAM_ERR_UNSUPPORTED;
+        if (dense) {
+            const int ms = dense_mxfp4_min_slices(*cfg);
+            if (ms > kMaxKSplit || cfg->inter % (ms * 512) != 0) return BEAM_ERR_UNSUPPORTED;
+        } else if (cfg->inter > kMxfp4PrefillMaxKd) {
+            return BEAM_ERR_UNSUPPORTED;
+        }
+    }
+    // above it, FP8 tiles hold the K-block scale codes of one reduction in LDS
+    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 && T > stream_max &&
+        (cfg->hidden > kFp8PrefillMaxKd || cfg->inter > kFp8PrefillMaxKd))
         return BEAM_ERR_UNSUPPORTED;
     return BEAM_OK;
 }
@@ -359,7 +427,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int64_t T, const void* x, const
         x_exp = at<void>(ws, L.x8);
         x_exp_scale = at<float>(ws, L.x8s);
     }
-    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids);
+    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids, at<void>(ws, L.yperm));
     Bracket b(BEAM_KERNEL_COMBINE, st);
     launch_combine(st, T, cfg->hidden, cfg->topk, cfg->weight_dtype == BEAM_DTYPE_F32, at<void>(ws, L.yperm),
                    at<int32_t>(ws, L.row_of_pair), wts, y);
@@ -396,7 +464,7 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, co
                true);
     const void* x_exp = fp8 ? at<void>(ws, L.x8) : at<void>(ws, L.x16);
     const float* x_exp_scale = fp8 ? at<float>(ws, L.x8s) : nullptr;
-    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids);
+    run_experts(*cfg, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, ids, at<void>(ws, L.yperm));
     // c1 = sqrt((k-1)/k), c2 = 1/sqrt(k), each computed in double and rounded once
     const double k = static_cast<double>(step_k);
     const float c1 = static_cast<float>(sqrt((k - 1.0) / k));
@@ -405,6 +473,115 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, co
     launch_post_residual(st, T, H, cfg->topk, at<uint16_t>(ws, L.yperm), at<int32_t>(ws, L.row_of_pair), wts,
                          post_gain, cfg->norm_eps, c1, c2, static_cast<uint16_t*>(h),
                          static_cast<uint16_t*>(moe_out));
+    return launch_status();
+}
+
+// The dense MLP runs on the MoE machinery as one expert that every token picks once
+// with weight 1; of cfg only hidden, inter, act_dtype, weight_dtype, fp8_block and
+// norm_eps are read.
+static beam_moe_config dense_view(const beam_moe_config* cfg) {
+    beam_moe_config c = *cfg;
+    c.n_experts = 1;
+    c.n_groups = 1;
+    c.topk_groups = 1;
+    c.topk = 1;
+    c.routed_scale = 1.0f;
+    return c;
+}
+
+static bool dense_config_valid(const beam_moe_config* c) {
+    if (!c) return false;
+    if (c->hidden < 1 || c->inter < 1) return false;
+    if (c->act_dtype < BEAM_DTYPE_F32 || c->act_dtype > BEAM_DTYPE_FP8_E4M3) return false;
+    if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_MXFP4) return false;
+    if (!(c->norm_eps >= 0.0f) || !isfinite(c->norm_eps)) return false;
+    return true;
+}
+
+static int check_dense(const beam_moe_config* cfg, int64_t T) {
+    if (!dense_config_valid(cfg) || T < 0 || T > INT32_MAX / 2) return BEAM_ERR_INVALID_ARG;
+    const beam_moe_config c = dense_view(cfg);
+    if (!gemm_supported(&c)) return BEAM_ERR_UNSUPPORTED;
+    return BEAM_OK;
+}
+
+static int check_dense_ws(const beam_moe_config& c, int64_t T, void* ws, size_t ws_bytes) {
+    if (!ws || ws_bytes < make_layout(c, T, true).total) return BEAM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return BEAM_ERR_INVALID_ARG;
+    return BEAM_OK;
+}
+
+static void dense_tables(int64_t T, const Layout& L, void* ws, hipStream_t st) {
+    launch_dense_setup(st, T, L.bm, at<int32_t>(ws, L.ids), at<int32_t>(ws, L.exp_cnt), at<int32_t>(ws, L.exp_off),
+                       at<int2>(ws, L.tiles), at<int32_t>(ws, L.meta), at<int32_t>(ws, L.active),
+                       at<int32_t>(ws, L.row_of_pair), at<int32_t>(ws, L.pair_of_row), at<float>(ws, L.wts));
+}
+
+size_t beam_dense_workspace_size(const beam_moe_config* cfg, int64_t T) {
+    if (!dense_config_valid(cfg) || T < 0 || T > INT32_MAX / 2) return 0;
+    return make_layout(dense_view(cfg), T, true).total;
+}
+
+int beam_dense_forward(const beam_moe_config* cfg, int64_t T, const void* x, const void* w13,
+                       const void* w13_scale, const void* w2, const void* w2_scale, void* y, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int s = check_dense(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (T == 0) return BEAM_OK;
+    if (!x || !y) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y)) return BEAM_ERR_INVALID_ARG;
+    const beam_moe_config c = dense_view(cfg);
+    if ((s = check_weights(&c, T, w13, w13_scale, w2, w2_scale, true)) != BEAM_OK) return s;
+    if ((s = check_dense_ws(c, T, ws, ws_bytes)) != BEAM_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = make_layout(c, T, true);
+    clear_hip_error();
+    dense_tables(T, L, ws, st);
+    const void* x_exp = x;
+    const float* x_exp_scale = nullptr;
+    if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3 || c.weight_dtype == BEAM_DTYPE_MXFP4) {
+        launch_quant_rows_fp8(st, T, c.hidden, true, x, at<uint8_t>(ws, L.x8), at<float>(ws, L.x8s));
+        x_exp = at<void>(ws, L.x8);
+        x_exp_scale = at<float>(ws, L.x8s);
+    }
+    run_experts(c, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, at<int32_t>(ws, L.ids), y, true);
+    return launch_status();
+}
+
+int beam_dense_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, const float* pre_gain,
+                                const float* post_gain, int32_t step_k, const void* w13, const void* w13_scale,
+                                const void* w2, const void* w2_scale, void* mlp_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+    int s = check_dense(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (cfg->act_dtype != BEAM_DTYPE_BF16) return BEAM_ERR_UNSUPPORTED;
+    if (step_k < 2) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!h) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(h) || (mlp_out && !aligned16(mlp_out))) return BEAM_ERR_INVALID_ARG;
+    const beam_moe_config c = dense_view(cfg);
+    if ((s = check_weights(&c, T, w13, w13_scale, w2, w2_scale, true)) != BEAM_OK) return s;
+    if ((s = check_dense_ws(c, T, ws, ws_bytes)) != BEAM_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = make_layout(c, T, true);
+    clear_hip_error();
+    dense_tables(T, L, ws, st);
+    const bool fp8 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3 || c.weight_dtype == BEAM_DTYPE_MXFP4;
+    const int H = c.hidden;
+    launch_prenorm(st, T, H, static_cast<const uint16_t*>(h), pre_gain, c.norm_eps, nullptr,
+                   fp8 ? nullptr : at<uint16_t>(ws, L.x16), fp8 ? at<uint8_t>(ws, L.x8) : nullptr,
+                   fp8 ? at<float>(ws, L.x8s) : nullptr);
+    const void* x_exp = fp8 ? at<void>(ws, L.x8) : at<void>(ws, L.x16);
+    const float* x_exp_scale = fp8 ? at<float>(ws, L.x8s) : nullptr;
+    run_experts(c, T, L, ws, st, x_exp, x_exp_scale, w13, w13_scale, w2, w2_scale, at<int32_t>(ws, L.ids),
+                at<void>(ws, L.yperm), true);
+    const double k = static_cast<double>(step_k);
+    const float c1 = static_cast<float>(sqrt((k - 1.0) / k));
+    const float c2 = static_cast<float>(1.0 / sqrt(k));
+    Bracket b(BEAM_KERNEL_COMBINE, st);
+    launch_post_residual(st, T, H, 1, at<uint16_t>(ws, L.yperm), at<int32_t>(ws, L.row_of_pair),
+                         at<float>(ws, L.wts), post_gain, c.norm_eps, c1, c2, static_cast<uint16_t*>(h),
+                         static_cast<uint16_t*>(mlp_out));
     return launch_status();
 }
 

@@ -286,4 +286,103 @@ void launch_post_residual(hipStream_t st, int64_t T, int H, int K, const uint16_
                                                              moe_out);
 }
 
+
+// ---------------------------------------------------------------------------
+// split-K reduction: out[i] = BF16(part[0][i] + ... + part[S-1][i]), slices added in
+// ascending order in FP32; 8 elements per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void splitk_reduce(int S, int64_t n, int64_t slice, const float* __restrict__ part,
+                                                     uint16_t* __restrict__ out) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    float v[8];
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(part + i);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(part + i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[j] = a0[j]; v[4 + j] = a1[j]; }
+    for (int z = 1; z < S; ++z) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(part + z * slice + i);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(part + z * slice + i + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[j] += b0[j]; v[4 + j] += b1[j]; }
+    }
+    *reinterpret_cast<u32x4*>(out + i) = pack_bf16x8(v);
+}
+
+void launch_splitk_reduce(hipStream_t st, int S, int64_t n, int64_t slice, const float* part, uint16_t* out) {
+    if (n == 0) return;
+    splitk_reduce<<<static_cast<unsigned>((n / 8 + 255) / 256), 256, 0, st>>>(S, n, slice, part, out);
+}
+
+// split-K SwiGLU: h[r, c] = BF16(SiLU(g) * u), g and u the ascending-order FP32 sums of
+// the slices' gate and up partials (part rows: n gate sums, then n up sums); 8 columns
+// per thread.
+__global__ __launch_bounds__(256) void splitk_swiglu(int S, int64_t rows, int n, int64_t slice,
+                                                     const float* __restrict__ part, uint16_t* __restrict__ h) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+    if (i >= rows * n) return;
+    const int64_t r = i / n;
+    const int c = static_cast<int>(i - r * n);
+    const float* pg = part + r * 2 * n + c;
+    float gs[8], us[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { gs[j] = 0.0f; us[j] = 0.0f; }
+    for (int z = 0; z < S; ++z) {
+        const float* p = pg + z * slice;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(p), g1 = *reinterpret_cast<const f32x4*>(p + 4);
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(p + n), u1 = *reinterpret_cast<const f32x4*>(p + n + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gs[j] += g0[j]; gs[4 + j] += g1[j];
+            us[j] += u0[j]; us[4 + j] += u1[j];
+        }
+    }
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = silu(gs[j]) * us[j];
+    *reinterpret_cast<u32x4*>(h + i) = pack_bf16x8(v);
+}
+
+void launch_splitk_swiglu(hipStream_t st, int S, int64_t rows, int n, int64_t slice, const float* part,
+                          uint16_t* h) {
+    const int64_t total = rows * n;
+    if (total == 0) return;
+    splitk_swiglu<<<static_cast<unsigned>((total / 8 + 255) / 256), 256, 0, st>>>(S, rows, n, slice, part, h);
+}
+
+// ---------------------------------------------------------------------------
+// routing tables of the dense MLP: every token is one row of the single "expert" 0, in
+// token order, with combine weight 1
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dense_setup(int64_t T, int BM, int32_t* ids, int32_t* exp_cnt,
+                                                   int32_t* exp_off, int2* tiles, int32_t* meta, int32_t* active,
+                                                   int32_t* row_of_pair, int32_t* pair_of_row, float* wts) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int n = static_cast<int>(T);
+    const int nt = expert_tile_count(n, BM);
+    if (t < T) {
+        ids[t] = 0;
+        row_of_pair[t] = static_cast<int32_t>(t);
+        pair_of_row[t] = static_cast<int32_t>(t);
+        wts[t] = 1.0f;
+    }
+    if (t < nt) tiles[t] = make_int2(0, static_cast<int>(t));
+    if (t == 0) {
+        exp_cnt[0] = n;
+        exp_off[0] = 0;
+        exp_off[1] = n;
+        active[0] = 0;
+        meta[kMetaTiles] = nt;
+        meta[kMetaActive] = 1;
+    }
+}
+
+void launch_dense_setup(hipStream_t st, int64_t T, int BM, int32_t* ids, int32_t* exp_cnt, int32_t* exp_off,
+                        int2* tiles, int32_t* meta, int32_t* active, int32_t* row_of_pair, int32_t* pair_of_row,
+                        float* wts) {
+    if (T == 0) return;
+    dense_setup<<<static_cast<unsigned>((T + 255) / 256), 256, 0, st>>>(T, BM, ids, exp_cnt, exp_off, tiles, meta,
+                                                                       active, row_of_pair, pair_of_row, wts);
+}
+
 }  // namespace beam

@@ -8,10 +8,11 @@
 // Rows r are the token->expert pairs sorted by expert, so each expert's rows are one
 // contiguous range [exp_off[e], exp_off[e] + exp_cnt[e]).
 //
-// One block per (active expert, 64 output columns for gate/up, 128 for down); each wave
-// streams 32 weight rows (16 gate + 16 up, or 32 down rows) straight from HBM into MFMA
-// B operands with deep unrolling, and the expert's activation rows ride along as the A
-// operand, 16 or 32 at a time (rows beyond the expert's count issue no loads).
+// One block per (active expert, 64 output columns for gate/up, 128 for down, K slice);
+// each wave streams 32 weight rows (16 gate + 16 up, or 32 down rows) straight from HBM
+// into MFMA B operands with deep unrolling, and the expert's activation rows ride along
+// as the A operand, 16 or 32 at a time (rows beyond the expert's count issue no loads).
+// The GEMMs of a single weight set split K over blockIdx.z (FP32 partial sums).
 // v_mfma_f32_16x16x32_bf16.
 #include "common.cuh"
 #include "kernels.h"
@@ -41,6 +42,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
                          (static_cast<int64_t>(e) * nw + n0 + ln) * g.kd + lq * 8;
     const uint16_t* wu = wp + static_cast<int64_t>(MODE == kGateUp ? g.n_out : 16) * g.kd;
     uint16_t* out = static_cast<uint16_t*>(g.out);
+    const int klen = g.kd / static_cast<int>(gridDim.z);          // this block's K slice
+    const int kbeg = static_cast<int>(blockIdx.z) * klen;
 
     // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up
     // to 16 R rows stream their weights once.
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
         f32x4 acc0[R], acc1[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        for (int k = 0; k < g.kd; k += 32 * U) {
+        for (int k = kbeg; k < kbeg + klen; k += 32 * U) {
             u32x4 b0[U], b1[U], a[R][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) b0[u] = *reinterpret_cast<const u32x4*>(wp + k + u * 32);
@@ -87,8 +90,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
                 const int mm = m0 + 16 * r + lq * 4 + i;
                 if (mm >= rows) continue;
                 uint16_t* orow = out + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
-                if (MODE == kGateUp) {
+                if (MODE == kGateUp && gridDim.z > 1) {
+                    float* prow = g.part + blockIdx.z * g.part_slice + static_cast<int64_t>(row0 + mm) * 2 * g.n_out + n0 + ln;
+                    prow[0] = acc0[r][i];
+                    prow[g.n_out] = acc1[r][i];
+                } else if (MODE == kGateUp) {
                     orow[0] = f32_to_bf16_bits(silu(acc0[r][i]) * acc1[r][i]);
+                } else if (gridDim.z > 1) {
+                    float* prow = g.part + blockIdx.z * g.part_slice + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
+                    prow[0] = acc0[r][i];
+                    prow[16] = acc1[r][i];
                 } else {
                     orow[0] = f32_to_bf16_bits(acc0[r][i]);
                     orow[16] = f32_to_bf16_bits(acc1[r][i]);
@@ -97,11 +108,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_decode(GroupedGemmArgs g) {
     }
 }
 
-void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
-    if (g.max_active == 0) return;
+int launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return 1;
     const int cols_per_block = (mode == kGateUp) ? 64 : 128;     // n_out is a multiple of 32
-    dim3 grid((g.n_out + cols_per_block - 1) / cols_per_block, g.max_active);
-    const bool u8 = (g.kd % 256) == 0;
+    const int nx = (g.n_out + cols_per_block - 1) / cols_per_block;
+    const int64_t out_elems = static_cast<int64_t>(g.max_rows) * g.n_out * (mode == kGateUp ? 2 : 1);
+    const int ks = g.part ? decode_k_split(static_cast<int64_t>(nx) * g.max_active, g.kd, 256, out_elems, g.part_cap) : 1;
+    dim3 grid(nx, g.max_active, ks);
+    const bool u8 = ((g.kd / ks) % 256) == 0;
     const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
 #define BEAM_DEC(M, GA, U) \
     do { if (r2) gemm_bf16_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
@@ -114,6 +128,7 @@ void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArg
         else          { if (u8) BEAM_DEC(kDown, false, 8); else BEAM_DEC(kDown, false, 1); }
     }
 #undef BEAM_DEC
+    return ks;
 }
 
 }  // namespace beam

@@ -51,6 +51,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
     const float* swg = wsc + (static_cast<int64_t>(e) * (nw / 128) + n0 / 128) * kb_n;
     const float* swu = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + n0) / 128) * kb_n;
     uint16_t* out = static_cast<uint16_t*>(g.out);
+    // this block's K slice (the GEMMs of a single weight set split K over blockIdx.z)
+    const int klen = g.kd / static_cast<int>(gridDim.z);
+    const int kbeg = static_cast<int>(blockIdx.z) * klen;
 
     // R row tiles of 16 per pass: each weight fragment feeds R MFMAs, so experts with up
     // to 16 R rows stream their weights once.
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
         f32x4 acc0[R], acc1[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) { acc0[r] = f32x4{0.f, 0.f, 0.f, 0.f}; acc1[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        for (int k = 0; k < g.kd; k += 128 * U) {
+        for (int k = kbeg; k < kbeg + klen; k += 128 * U) {
             u32x4 b0[U][2], b1[U][2], a[R][U][2];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -120,16 +123,27 @@ __global__ __launch_bounds__(256) void gemm_fp8_decode(GroupedGemmArgs g) {
                 if (mm >= rows) continue;
                 const int64_t ar = GATHER ? g.pair_of_row[row0 + mm] / g.topk : static_cast<int64_t>(row0 + mm);
                 const float sa = g.a_scale[ar];
+                if (gridDim.z > 1) {
+                    // FP32 partial sums: gate then up sums for gate/up (SwiGLU after the reduction)
+                    const int64_t o = static_cast<int64_t>(row0 + mm) * (MODE == kGateUp ? 2 * g.n_out : g.ldo) + n0 + ln;
+                    float* pz = g.part + blockIdx.z * g.part_slice;
+                    pz[o] = acc0[r][i] * sa;
+                    if (MODE == kGateUp) pz[o + g.n_out] = acc1[r][i] * sa;
+                    continue;
+                }
                 const float v = (MODE == kGateUp) ? silu(acc0[r][i] * sa) * (acc1[r][i] * sa) : acc0[r][i] * sa;
                 out[static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln] = f32_to_bf16_bits(v);
             }
     }
 }
 
-void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
-    if (g.max_active == 0) return;
-    dim3 grid((g.n_out + 63) / 64, g.max_active);
-    const bool u4 = (g.kd % 512) == 0;
+int launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return 1;
+    const int nx = (g.n_out + 63) / 64;
+    const int64_t out_elems = static_cast<int64_t>(g.max_rows) * g.n_out * (mode == kGateUp ? 2 : 1);
+    const int ks = g.part ? decode_k_split(static_cast<int64_t>(nx) * g.max_active, g.kd, 512, out_elems, g.part_cap) : 1;
+    dim3 grid(nx, g.max_active, ks);
+    const bool u4 = ((g.kd / ks) % 512) == 0;
     const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
 #define BEAM_DEC(M, GA, U) \
     do { if (r2) gemm_fp8_decode<M, GA, U, 2><<<grid, 256, 0, st>>>(g); \
@@ -142,6 +156,7 @@ void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs
         else          { if (u4) BEAM_DEC(kDown, false, 4); else BEAM_DEC(kDown, false, 1); }
     }
 #undef BEAM_DEC
+    return ks;
 }
 
 }  // namespace beam

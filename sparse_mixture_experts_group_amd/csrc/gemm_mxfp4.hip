@@ -78,6 +78,9 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
         sp[t] = sc + rr * srow_b;
     }
     uint16_t* out = static_cast<uint16_t*>(g.out);
+    // this block's K slice (the GEMMs of a single weight set split K over blockIdx.z)
+    const int klen = g.kd / static_cast<int>(gridDim.z);
+    const int kbeg = static_cast<int>(blockIdx.z) * klen;
 
     for (int m0 = 0; m0 < rows; m0 += 16 * R) {
         bool mv[R];
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int t = 0; t < NS; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < g.kd; k += 128 * U) {
+        for (int k = kbeg; k < kbeg + klen; k += 128 * U) {
             u32x4 b[NS][U], a[R][U][2];
             // E8M0 scales of blocks k/32 + 4u + lq: byte lq of dword u of 4U bytes
             uint32_t s[NS][U];
@@ -148,10 +151,22 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
                 const int64_t ar = GATHER ? g.pair_of_row[row0 + mm] / g.topk : static_cast<int64_t>(row0 + mm);
                 const float sa = g.a_scale[ar];
                 uint16_t* orow = out + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
-                if (MODE == kGateUp) {
+                if (MODE == kGateUp && gridDim.z > 1) {
+                    // FP32 partial sums: gate then up sums (SwiGLU after the reduction)
+                    float* prow = g.part + blockIdx.z * g.part_slice + static_cast<int64_t>(row0 + mm) * 2 * g.n_out + n0 + ln;
+#pragma unroll
+                    for (int j = 0; j < NS / 2; ++j) {
+                        prow[16 * j] = acc[r][2 * j][i] * sa;
+                        prow[g.n_out + 16 * j] = acc[r][2 * j + 1][i] * sa;
+                    }
+                } else if (MODE == kGateUp) {
 #pragma unroll
                     for (int j = 0; j < NS / 2; ++j)
                         orow[16 * j] = f32_to_bf16_bits(silu(acc[r][2 * j][i] * sa) * (acc[r][2 * j + 1][i] * sa));
+                } else if (gridDim.z > 1) {
+                    float* prow = g.part + blockIdx.z * g.part_slice + static_cast<int64_t>(row0 + mm) * g.ldo + n0 + ln;
+#pragma unroll
+                    for (int t = 0; t < NS; ++t) prow[16 * t] = acc[r][t][i] * sa;
                 } else {
 #pragma unroll
                     for (int t = 0; t < NS; ++t) orow[16 * t] = f32_to_bf16_bits(acc[r][t][i] * sa);
@@ -160,13 +175,17 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_decode(GroupedGemmArgs g) {
     }
 }
 
-void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
-    if (g.max_active == 0) return;
+int launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_active == 0) return 1;
     constexpr int NS = kMxfp4Streams;
     const int cols_per_block = 4 * ((mode == kGateUp) ? 8 * NS : 16 * NS);   // n_out: multiple of it
-    dim3 grid((g.n_out + cols_per_block - 1) / cols_per_block, g.max_active);
-    // K blocks of 128 per iteration: as many as divide the reduction
-    const int u = (g.kd % (128 * kMxfp4U) == 0) ? kMxfp4U : ((g.kd % 512 == 0) ? 4 : 1);
+    const int nx = (g.n_out + cols_per_block - 1) / cols_per_block;
+    const int64_t out_elems = static_cast<int64_t>(g.max_rows) * g.n_out * (mode == kGateUp ? 2 : 1);
+    const int ks = g.part ? decode_k_split(static_cast<int64_t>(nx) * g.max_active, g.kd, 512, out_elems, g.part_cap) : 1;
+    dim3 grid(nx, g.max_active, ks);
+    // K blocks of 128 per iteration: as many as divide the slice
+    const int klen = g.kd / ks;
+    const int u = (klen % (128 * kMxfp4U) == 0) ? kMxfp4U : ((klen % 512 == 0) ? 4 : 1);
     const bool r2 = g.max_rows > 16;      // an expert can hold more than 16 rows
 #define BEAM_DEC_U(M, GA, U) \
     do { if (r2) gemm_mxfp4_decode<M, GA, U, 2, NS><<<grid, 256, 0, st>>>(g); \
@@ -183,6 +202,7 @@ void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmAr
     }
 #undef BEAM_DEC_U
 #undef BEAM_DEC
+    return ks;
 }
 
 }  // namespace beam

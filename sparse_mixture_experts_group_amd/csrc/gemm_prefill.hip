@@ -36,10 +36,14 @@ template <int WT> constexpr int b_row_bytes() { return WT == kWtMxfp4 ? 32 : kSt
 template <int WT> constexpr int stage_bytes() { return kPrefillBM * kStageRowBytes + 256 * b_row_bytes<WT>(); }
 constexpr int kStages = 4;
 constexpr int kMxfp4MaxKd = 8192;               // LDS holds the block's 256 x kd/32 scales
+constexpr int kFp8MaxKb = kFp8PrefillMaxKd / 128;   // FP8: K blocks of a reduction
+// LDS after the stages: MXFP4 block scales (256 rows x kd/32 codes), or for FP8 with more
+// than 64 K blocks two rows of kd/128 block-scale codes
 template <int WT> constexpr size_t lds_bytes_max() {
-    return kStages * stage_bytes<WT>() + (WT == kWtMxfp4 ? 256 * (kMxfp4MaxKd / 32) : 0);
+    return kStages * stage_bytes<WT>() +
+           (WT == kWtMxfp4 ? 256 * (kMxfp4MaxKd / 32) : (WT == kWtFp8 ? 2 * kFp8MaxKb : 0));
 }
-static_assert(lds_bytes_max<kWtBf16>() <= 160 * 1024 && lds_bytes_max<kWtMxfp4>() <= 160 * 1024, "LDS budget");
+static_assert(lds_bytes_max<kWtFp8>() <= 160 * 1024 && lds_bytes_max<kWtMxfp4>() <= 160 * 1024, "LDS budget");
 
 // FP4 rows of 32 bytes: chunk c of row r in slot c ^ ((r >> 3) & 1), so the 16 rows one
 // fragment read serves per LDS cycle cover all banks.
@@ -79,7 +83,13 @@ template <> struct StageFrags<kWtMxfp4> { i32x8 a[4]; u32x4 b[4]; };
 // from registers while reading the fragments of stage j + 1 and loading stage j + 4
 // into the slot of stage j, whose fragments were read in the previous iteration.  So
 // three stages are in flight while one is computed.
-template <int MODE, bool GATHER, int WT>
+//
+// SPLIT: the GEMMs of a single weight set, which alone have too few tiles for the chip,
+// split K into g.k_slices slices and write FP32 partial sums.  The 1-D grid enumerates
+// (row tile, column tile, slice) with the slice fastest and no XCD grouping, so
+// consecutive blocks -- which the dispatcher deals out over the XCDs in turn -- spread
+// the few tiles over the whole chip.
+template <int MODE, bool GATHER, int WT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     constexpr int BM = kPrefillBM, BN = 256, MI = 4, NST = kStages;
     constexpr bool Q8 = WT != kWtBf16;                  // E4M3 activations with row scales
@@ -90,8 +100,16 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
     const int n_tiles_n = g.n_out / NCOL;
-    int tile, nt;
-    prefill_tile_of_block(n_tiles_n, g.group_m, tile, nt);
+    int tile, nt, kz = 0;
+    if constexpr (SPLIT) {
+        const int lin = blockIdx.x;
+        kz = lin % g.k_slices;
+        const int rest = lin / g.k_slices;
+        nt = rest % n_tiles_n;
+        tile = rest / n_tiles_n;
+    } else {
+        prefill_tile_of_block(n_tiles_n, g.group_m, tile, nt);
+    }
     if (tile >= g.meta[kMetaTiles]) return;
     const int2 ti = g.tiles[tile];                     // (expert, tile of the expert)
     const int e = ti.x, n_e = g.exp_cnt[e];
@@ -104,6 +122,10 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     // bytes per weight row (MXFP4: two values per byte)
     const int64_t krow = (WT == kWtMxfp4) ? g.kd / 2 : static_cast<int64_t>(g.kd) * EB;
+    // K slice of this block
+    const int klen = SPLIT ? g.kd / g.k_slices : g.kd;
+    const int kbeg = SPLIT ? kz * klen : 0;
+    const int64_t kbeg_w = (WT == kWtMxfp4) ? kbeg / 2 : static_cast<int64_t>(kbeg) * EB;   // weight bytes
 
     // MFMA row tiles of this wave that hold rows of the expert (wave-uniform; a prefix of
     // the wave's tiles): the others skip their loads, LDS reads and MFMAs.
@@ -121,7 +143,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     for (int i = 0; i < MI; ++i) {
         const int rr = min((wm + 2 * i) * 32 + 16 * wn + dr, rows - 1);
         const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
-        ag[i] = static_cast<const uint8_t*>(g.a) + arow * g.lda * EB + soff;
+        ag[i] = static_cast<const uint8_t*>(g.a) + (arow * g.lda + kbeg) * EB + soff;
     }
     // B rows of wave w are affine in j (for gate/up, waves 0-1 move gate rows, 2-3 up rows).
     // BF16 / FP8: rows w*64 + 16 j + lane/4, lane i fetching the chunk of LDS slot i % 4;
@@ -135,36 +157,48 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         return c0 + r;
     };
     const uint8_t* bg = static_cast<const uint8_t*>(g.w) +
-                        (static_cast<int64_t>(e) * nw + weight_row(wave * 64 + bdr)) * krow + bsoff;
+                        (static_cast<int64_t>(e) * nw + weight_row(wave * 64 + bdr)) * krow + kbeg_w + bsoff;
     const int64_t bstep = BRPI * krow;    // bytes between B rows j and j + 1
 
     // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l (gate-column
     // block in s_lo, up-column block in s_hi for gate/up; this wave's column block for
-    // down).  kd / 128 <= 64 K blocks (hidden and inter are at most 8192).
+    // down).  Blocks from 64 on are read from LDS (see below).
     int s_lo = kUnitScale, s_hi = kUnitScale;
+    uint8_t* fsc = smem + NST * SB;          // FP8, kd / 128 > 64: [2][kd / 128] codes
     if constexpr (WT == kWtFp8) {
-        const int kb_n = g.kd / 128;
+        const int kb_all = g.kd / 128, kb_n = klen / 128;     // K blocks of the row, of the slice
         const float* r_lo;
         const float* r_hi;
-        const float* wsc = static_cast<const float*>(g.w_scale);
+        const float* wsc = static_cast<const float*>(g.w_scale) + kbeg / 128;
         if (MODE == kGateUp) {
-            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_n;
-            r_hi = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_n;
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_all;
+            r_hi = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_all;
         } else {
-            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_n;
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_all;
             r_hi = r_lo;
         }
         const int l = min(lane, kb_n - 1);
         s_lo = (__float_as_uint(r_lo[l]) >> 23) & 0xff;
         s_hi = (__float_as_uint(r_hi[l]) >> 23) & 0xff;
+        if (kb_n > 64) {
+            // the codes of every K block in LDS: row 0 the gate (down: wn = 0) column
+            // block, row 1 the up (down: wn = 1) block; waves 0 and 1 write them
+            if (wave < 2) {
+                const float* src = (MODE == kGateUp) ? (wave == 0 ? r_lo : r_hi) : r_lo;
+                for (int i = lane; i < kb_n; i += 64) fsc[wave * kb_n + i] = (__float_as_uint(src[i]) >> 23) & 0xff;
+            }
+            // complete before the pipeline: its waits count the direct-to-LDS loads alone
+            __syncthreads();
+        }
     }
-    // MXFP4 block scales: the block's 256 weight rows x kd/32 E8M0 codes, staged in LDS
-    // after the stages (thread t copies row t; the rows of one half are contiguous).
-    const int srow = g.kd / 32;
+    // MXFP4 block scales: the block's 256 weight rows x klen/32 E8M0 codes of its K slice,
+    // staged in LDS after the stages (thread t copies row t; the rows of one half are
+    // contiguous).
+    const int srow = klen / 32;
     uint8_t* ssc = smem + NST * SB;
     if constexpr (WT == kWtMxfp4) {
         const uint8_t* src = static_cast<const uint8_t*>(g.w_scale) +
-                             (static_cast<int64_t>(e) * nw + weight_row(tid)) * srow;
+                             (static_cast<int64_t>(e) * nw + weight_row(tid)) * (g.kd / 32) + kbeg / 32;
         for (int c = 0; c < srow; c += 16)
             *reinterpret_cast<u32x4*>(ssc + tid * srow + c) = *reinterpret_cast<const u32x4*>(src + c);
         // complete before the pipeline: its waits count the direct-to-LDS loads alone
@@ -188,7 +222,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
                                       : wn * 128 + i * 32 + l32;
     }
-    const int nk = g.kd / BK;          // even: hidden and inter are multiples of 2 * BK
+    const int nk = klen / BK;          // even: slices are multiples of 2 * BK
 
     // The K loop is instantiated per count MV of live row tiles, so no instance tests them.
     auto k_loop = [&](auto mv_tag) {
@@ -254,8 +288,15 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         auto mfma_stage = [&](const StageFrags<WT>& f, int kt) {
             if constexpr (WT == kWtFp8) {
                 const int kb = kt >> 1;                 // 128-wide K block of this stage
-                const int sc_lo = __builtin_amdgcn_readlane(s_lo, kb);
-                const int sc_hi = __builtin_amdgcn_readlane(s_hi, kb);
+                int sc_lo, sc_hi;
+                if (kb < 64) {
+                    sc_lo = __builtin_amdgcn_readlane(s_lo, kb);
+                    sc_hi = __builtin_amdgcn_readlane(s_hi, kb);
+                } else {
+                    const int kb_n = klen / 128;
+                    sc_lo = fsc[(MODE == kGateUp ? 0 : wn) * kb_n + kb];
+                    sc_hi = (MODE == kGateUp) ? fsc[kb_n + kb] : sc_lo;
+                }
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
                     if (mi < MV) {
@@ -340,6 +381,23 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                 sa = g.a_scale[ar];
             }
             uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
+            if constexpr (SPLIT) {
+                // FP32 partial sums of the slice: gate then up sums for gate/up (the SwiGLU
+                // follows the reduction)
+                float* prow = g.part + kz * g.part_slice +
+                              static_cast<int64_t>(row0 + m) * (MODE == kGateUp ? 2 * g.n_out : g.ldo);
+                if (MODE == kGateUp) {
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        prow[c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni][i] * sa;
+                        prow[g.n_out + c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni + 2][i] * sa;
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) prow[c0 + wn * 128 + ni * 32 + l32] = acc[mi][ni][i] * sa;
+                }
+                continue;
+            }
             if (MODE == kGateUp) {
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
@@ -354,38 +412,68 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     }
 }
 
-template <int MODE, bool GATHER, int WT>
-static void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks) {
+template <int MODE, bool GATHER, int WT, bool SPLIT>
+static void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
     static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT, SPLIT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes_max<WT>()));
         attr_set = true;
     }
-    const size_t lds = kStages * stage_bytes<WT>() + (WT == kWtMxfp4 ? 256 * static_cast<size_t>(g.kd / 32) : 0);
-    gemm_prefill<MODE, GATHER, WT><<<blocks, 256, lds, st>>>(g);
-}
-
-template <int WT>
-static void launch_prefill_dtype(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks) {
-    if (mode == kGateUp) {
-        if (g.gather) launch_prefill_inst<kGateUp, true, WT>(st, g, blocks);
-        else launch_prefill_inst<kGateUp, false, WT>(st, g, blocks);
+    const int klen = g.kd / ks;
+    size_t extra = 0;
+    if (WT == kWtMxfp4) extra = 256 * static_cast<size_t>(klen / 32);
+    if (WT == kWtFp8 && klen / 128 > 64) extra = 2 * static_cast<size_t>(klen / 128);
+    const size_t lds = kStages * stage_bytes<WT>() + extra;
+    if (SPLIT) {
+        GroupedGemmArgs gs = g;
+        gs.k_slices = ks;
+        gemm_prefill<MODE, GATHER, WT, SPLIT><<<blocks, 256, lds, st>>>(gs);
     } else {
-        if (g.gather) launch_prefill_inst<kDown, true, WT>(st, g, blocks);
-        else launch_prefill_inst<kDown, false, WT>(st, g, blocks);
+        gemm_prefill<MODE, GATHER, WT, SPLIT><<<blocks, 256, lds, st>>>(g);
     }
 }
 
-void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt) {
-    if (g.max_tiles == 0) return;
+template <int WT>
+static void launch_prefill_dtype(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks, int ks) {
+    // split K only for a single weight set (rows in token order, no gather); the grid
+    // enumerates every (row tile bound, column tile, slice)
+    if (ks > 1) {
+        const int ncol = (mode == kGateUp) ? 128 : 256;
+        const int nb = g.max_tiles * (g.n_out / ncol) * ks;
+        if (mode == kGateUp) launch_prefill_inst<kGateUp, false, WT, true>(st, g, nb, ks);
+        else launch_prefill_inst<kDown, false, WT, true>(st, g, nb, ks);
+    } else if (mode == kGateUp) {
+        if (g.gather) launch_prefill_inst<kGateUp, true, WT, false>(st, g, blocks, 1);
+        else launch_prefill_inst<kGateUp, false, WT, false>(st, g, blocks, 1);
+    } else {
+        if (g.gather) launch_prefill_inst<kDown, true, WT, false>(st, g, blocks, 1);
+        else launch_prefill_inst<kDown, false, WT, false>(st, g, blocks, 1);
+    }
+}
+
+int prefill_k_split(GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt) {
+    if (!g.part || g.gather) return 1;
+    const int ncol = (mode == kGateUp) ? 128 : 256;
+    const int64_t out_elems = static_cast<int64_t>(g.max_rows) * g.n_out * (mode == kGateUp ? 2 : 1);
+    int ks = decode_k_split(static_cast<int64_t>(g.max_tiles) * (g.n_out / ncol), g.kd, 512, out_elems, g.part_cap);
+    // MXFP4: a slice's weight scales must fit in LDS
+    if (wt == PrefillWeights::kMxfp4)
+        while (g.kd / ks > kMxfp4PrefillMaxKd) ks *= 2;
+    return ks;
+}
+
+int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt) {
+    if (g.max_tiles == 0) return 1;
     const int ncol = (mode == kGateUp) ? 128 : 256;
     // every (row tile, column tile) of whole groups of group_m row tiles, in whole XCD chunks
     const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
     const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
-    if (wt == PrefillWeights::kFp8) launch_prefill_dtype<kWtFp8>(st, mode, g, blocks);
-    else if (wt == PrefillWeights::kMxfp4) launch_prefill_dtype<kWtMxfp4>(st, mode, g, blocks);
-    else launch_prefill_dtype<kWtBf16>(st, mode, g, blocks);
+    const int ks = prefill_k_split(mode, g, wt);
+    if (wt == PrefillWeights::kFp8) launch_prefill_dtype<kWtFp8>(st, mode, g, blocks, ks);
+    else if (wt == PrefillWeights::kMxfp4) launch_prefill_dtype<kWtMxfp4>(st, mode, g, blocks, ks);
+    else launch_prefill_dtype<kWtBf16>(st, mode, g, blocks, ks);
+    return ks;
 }
 
 }  // namespace beam

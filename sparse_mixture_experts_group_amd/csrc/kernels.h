@@ -27,6 +27,7 @@ __host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
     return static_cast<int>((j * m / nt) * 32);
 }
 constexpr int kDecodeMaxT = 256;    // token counts up to this use the streaming GEMMs
+constexpr int kDenseStreamMaxT = 32;   // the same for the dense MLP (all rows on one weight set)
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
 // chunk sums) below 4096 tokens, where it fills the chip and the tiled kernel cannot,
@@ -82,20 +83,46 @@ struct GroupedGemmArgs {
     int max_rows;             // bound on the rows of one expert (min(T, T*K))
     void* out;                // [rows, n_out]
     int64_t ldo;              // elements per output row
+    // Streaming GEMMs only: when non-null the launcher may split K over blockIdx.z (for a
+    // single weight set, whose GEMMs alone have too few column blocks to fill the chip);
+    // slice z then writes FP32 partial sums to part + z * part_slice instead of out: rows
+    // of n_out sums for down, of 2 n_out for gate/up (gate sums, then up sums; the SwiGLU
+    // is applied after the reduction).  part_cap bounds the floats of all slices.  The
+    // launcher returns the slice count.
+    float* part;
+    int64_t part_slice;
+    int64_t part_cap;
+    int k_slices;             // LDS-tiled GEMMs: K slices of a split launch (set by the launcher)
 };
+constexpr int kMaxKSplit = 16;
+
+// K slices for a streaming GEMM of `blocks` column blocks whose partial sums take
+// `out_elems` floats per slice: doubled while the grid holds fewer than four blocks per
+// CU, every slice stays a multiple of `step` (the kernel's widest K step) and the slices
+// fit in `cap` floats.
+inline int decode_k_split(int64_t blocks, int kd, int step, int64_t out_elems, int64_t cap) {
+    int s = 1;
+    while (s < kMaxKSplit && blocks * s < 1024 && kd % (2 * s * step) == 0 && 2 * s * out_elems <= cap) s *= 2;
+    return s;
+}
 
 // gemm_f32.hip (plain FP32, one thread per output)
 void launch_gemm_f32(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int64_t rows,
                      const int32_t* ids);
 // gemm_bf16_decode.hip / gemm_fp8.hip: few rows per expert, weight streaming
-void launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
-void launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// These return the number of K slices written to g.part (1: the result is in g.out).
+int launch_gemm_bf16_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+int launch_gemm_fp8_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 // gemm_mxfp4.hip: MXFP4 weights, E4M3 activations, weight streaming
-void launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+int launch_gemm_mxfp4_decode(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 // gemm_prefill.hip: 256 x 256 LDS-tiled MFMA, BF16, FP8 or MXFP4 weights
 enum class PrefillWeights { kBf16, kFp8, kMxfp4 };
 constexpr int kMxfp4PrefillMaxKd = 8192;    // LDS holds a tile's weight scales
-void launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
+constexpr int kFp8PrefillMaxKd = 32768;     // LDS holds the K-block scale codes past 64 blocks
+// Returns the number of K slices written to g.part (1: the result is in g.out), which
+// prefill_k_split gives beforehand.  MXFP4 slices hold at most kMxfp4PrefillMaxKd of K.
+int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
+int prefill_k_split(GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
 
 // elementwise.hip
 void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,
@@ -107,5 +134,16 @@ void launch_quant_rows_fp8(hipStream_t st, int64_t rows, int cols, bool src_bf16
 void launch_post_residual(hipStream_t st, int64_t T, int H, int K, const uint16_t* yperm,
                           const int32_t* row_of_pair, const float* w, const float* gain,
                           float eps, float c1, float c2, uint16_t* h, uint16_t* moe_out);
+// out[i] = BF16(part[0][i] + part[1][i] + ... + part[S-1][i]) for i < n (n % 8 == 0)
+void launch_splitk_reduce(hipStream_t st, int S, int64_t n, int64_t slice, const float* part, uint16_t* out);
+// h[r, c] = BF16(SiLU(sum_z part[z][r][c]) * sum_z part[z][r][n + c]) for r < rows, c < n
+// (n % 8 == 0; part rows of 2n floats)
+void launch_splitk_swiglu(hipStream_t st, int S, int64_t rows, int n, int64_t slice, const float* part,
+                          uint16_t* h);
+// Routing tables of a single weight set applied to every token (the dense MLP): one
+// "expert" 0 holding rows 0..T-1 in token order, unit combine weights.
+void launch_dense_setup(hipStream_t st, int64_t T, int BM, int32_t* ids, int32_t* exp_cnt, int32_t* exp_off,
+                        int2* tiles, int32_t* meta, int32_t* active, int32_t* row_of_pair, int32_t* pair_of_row,
+                        float* wts);
 
 }  // namespace beam

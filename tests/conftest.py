@@ -19,15 +19,20 @@ def pytest_configure(config):
 _CACHE = {}
 
 
-def gpu_inputs(name: str, T: int | None = None):
-    """Host inputs of a named workload plus their device copies (cached per session;
-    the Beam-shaped workloads share one weight draw per weight dtype)."""
+def gpu_inputs(name: str, T: int | None = None, **overrides):
+    """Host inputs of a named workload (fields replaced by `overrides`) plus their device
+    copies (cached per session; the Beam-shaped workloads share one weight draw per
+    weight dtype, the dense MLP has its own)."""
+    from dataclasses import replace
+
     import numpy as np
     import torch
     from beam_inputs import WORKLOADS, make_inputs
 
     w = WORKLOADS[name] if T is None else WORKLOADS[name].with_T(T)
-    key_w = (w.H, w.I, w.E, w.weight_dtype, w.seed)
+    if overrides:
+        w = replace(w, **overrides)
+    key_w = (w.H, w.I, w.E, w.weight_dtype, w.seed, w.dense)
     if key_w not in _CACHE:
         print(f"[inputs] generating weights for {name} ...", flush=True)
         full = make_inputs(w)
@@ -43,7 +48,7 @@ def gpu_inputs(name: str, T: int | None = None):
             dev["w2"] = torch.from_numpy(full.w2).cuda()
             dev["w13_scale"] = torch.from_numpy(full.w13_scale).cuda()
             dev["w2_scale"] = torch.from_numpy(full.w2_scale).cuda()
-        dev["w_router"] = torch.from_numpy(full.w_router).cuda()
+        dev["w_router"] = None if full.w_router is None else torch.from_numpy(full.w_router).cuda()
         _CACHE[key_w] = (full, dev)
         print(f"[inputs] weights for {name} resident on the GPU", flush=True)
     full, dev = _CACHE[key_w]

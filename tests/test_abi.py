@@ -16,7 +16,7 @@ FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: every call below fails
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(beam_(?:moe|dense)_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = bm.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert bm.abi_version() == 2
+    assert bm.abi_version() == 3
 
 
 def test_status_strings():
@@ -67,6 +67,7 @@ def test_invalid_config_rejected(kw):
 
 @pytest.mark.parametrize("kw", [dict(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_BF16),
                                 dict(hidden=5000), dict(inter=100), dict(n_experts=96, n_groups=32),
+                                dict(hidden=384),     # the prefill down GEMM tiles H by 256
                                 dict(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3, fp8_block=64)])
 def test_unsupported_config(kw):
     c = beam(**kw)
@@ -121,5 +122,79 @@ def test_route_and_sublayer_argument_errors():
         FAKE, ws_bytes, None)
     assert sub(c, 1, 1 << 40) == bm.BEAM_ERR_INVALID_ARG                 # step k must be >= 2
     assert sub(beam(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_F32), 10,
+               1 << 40) == bm.BEAM_ERR_UNSUPPORTED
+    assert sub(c, 10, 16) == bm.BEAM_ERR_WORKSPACE
+
+
+def test_fp8_reduction_bound_above_the_streaming_range():
+    """FP8 tiles keep the K-block scale codes of one reduction in LDS: K <= 32768."""
+    c = beam(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3, inter=32768 + 128)
+    fwd = lambda T: bm.lib().beam_moe_forward(ctypes.byref(c), T, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, None, None, FAKE, 1 << 40, None)
+    assert fwd(257) == bm.BEAM_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# dense MLP entry points
+# ---------------------------------------------------------------------------
+def test_dense_workspace_and_config_checks():
+    c = bm.make_dense_config()
+    n16, n4k = bm.beam_dense_workspace_size(c, 16), bm.beam_dense_workspace_size(c, 4096)
+    assert 0 < n16 < n4k
+    # h [T, I] BF16 and the [T, H] down output at least; no router regions
+    assert n4k >= 4096 * (20480 + 5120) * 2
+    assert n4k < bm.beam_moe_workspace_size(bm.make_config(), 4096) * 2
+    # split-K partial sums in the streaming range: up to 8 FP32 slices of [T, H]
+    assert n16 >= 8 * 16 * 5120 * 4
+    assert bm.beam_dense_workspace_size(c, -1) == 0
+    assert bm.beam_dense_workspace_size(bm.make_dense_config(hidden=0), 16) == 0
+    # the router fields are not read
+    odd = bm.make_dense_config()
+    odd.n_experts, odd.n_groups, odd.topk = 0, 0, 0
+    assert bm.beam_dense_workspace_size(odd, 16) == n16
+
+
+@pytest.mark.parametrize("kw,status", [(dict(hidden=0), bm.BEAM_ERR_INVALID_ARG),
+                                       (dict(act_dtype=9), bm.BEAM_ERR_INVALID_ARG),
+                                       (dict(norm_eps=float("inf")), bm.BEAM_ERR_INVALID_ARG),
+                                       (dict(hidden=384), bm.BEAM_ERR_UNSUPPORTED),
+                                       (dict(inter=100), bm.BEAM_ERR_UNSUPPORTED),
+                                       (dict(act_dtype=bm.BEAM_DTYPE_F32), bm.BEAM_ERR_UNSUPPORTED)])
+def test_dense_config_errors(kw, status):
+    c = bm.make_dense_config(**kw)
+    st = bm.lib().beam_dense_forward(ctypes.byref(c), 16, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 40, None)
+    assert st == status
+
+
+def test_dense_argument_errors_before_any_launch():
+    c = bm.make_dense_config()
+    L = bm.lib()
+    fwd = lambda T, x, y, ws, nb, w13=FAKE, s13=None, cfg=c: L.beam_dense_forward(
+        ctypes.byref(cfg), T, x, w13, s13, FAKE, None, y, ws, nb, None)
+    assert fwd(0, None, None, None, 0) == bm.BEAM_OK
+    assert fwd(-1, FAKE, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, None, FAKE, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, None, FAKE, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, FAKE, FAKE, 1 << 40, w13=None) == bm.BEAM_ERR_INVALID_ARG
+    assert fwd(16, FAKE, FAKE, FAKE, 1 << 40, s13=FAKE) == bm.BEAM_ERR_INVALID_ARG
+    need = bm.beam_dense_workspace_size(c, 16)
+    assert fwd(16, FAKE, FAKE, FAKE, need - 1) == bm.BEAM_ERR_WORKSPACE
+    # MXFP4 above the dense streaming range (32 tokens): the tiled kernels stage a K
+    # slice's weight scales in LDS (at most 8192 long), so the down GEMM of width 20480
+    # runs in 4 slices; hidden must stay <= 8192 and the width split into whole slices
+    c4 = bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4)
+    mx = lambda cfg, T, nb: L.beam_dense_forward(ctypes.byref(cfg), T, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 nb, None)
+    assert mx(c4, 33, 16) == bm.BEAM_ERR_WORKSPACE
+    assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, hidden=10240), 33, 1 << 40) == \
+        bm.BEAM_ERR_UNSUPPORTED
+    assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, inter=20608), 33, 1 << 40) == \
+        bm.BEAM_ERR_UNSUPPORTED
+    assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, inter=20608), 32, 16) == \
+        bm.BEAM_ERR_WORKSPACE
+    sub = lambda cfg, k, nb: L.beam_dense_sublayer_forward(ctypes.byref(cfg), 16, FAKE, None, None, k, FAKE,
+                                                           None, FAKE, None, None, FAKE, nb, None)
+    assert sub(c, 1, 1 << 40) == bm.BEAM_ERR_INVALID_ARG
+    assert sub(bm.make_dense_config(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_F32), 10,
                1 << 40) == bm.BEAM_ERR_UNSUPPORTED
     assert sub(c, 10, 16) == bm.BEAM_ERR_WORKSPACE

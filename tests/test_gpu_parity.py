@@ -316,3 +316,69 @@ def test_mxfp4_forward(name, T):
     err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
     print(f"[case] mxfp4 forward T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[DT_MXFP4]
+
+
+
+# ---------------------------------------------------------------------------
+# dense SwiGLU MLP (the first decoder layers): one weight set, every token
+# ---------------------------------------------------------------------------
+_DENSE_BANK = {}
+
+
+def dense_bank(w, full):
+    """Float64 weights of the dense MLP, decoded once per weight dtype."""
+    key = w.weight_dtype
+    if key not in _DENSE_BANK:
+        w13, w2 = bank_of(w, full).expert(0)
+        _DENSE_BANK[key] = oracle.ExpertBank(w13[None], w2[None], "f32")
+    return _DENSE_BANK[key]
+
+
+def dense_cfg(w):
+    return bm.make_dense_config(hidden=w.H, inter=w.I, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
+                                fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+
+
+@pytest.mark.parametrize("dt,T", [(DT_BF16, 16), (DT_BF16, 1), (DT_BF16, 32), (DT_BF16, 33), (DT_BF16, 200),
+                                  (DT_BF16, 700), (DT_BF16, 4096), (DT_FP8, 16), (DT_FP8, 200), (DT_FP8, 700),
+                                  (DT_MXFP4, 16), (DT_MXFP4, 32), (DT_MXFP4, 200), (DT_MXFP4, 4096)])
+def test_dense_forward(dt, T):
+    """Dense MLP through beam_dense_forward: streaming kernels with both GEMMs split
+    over K (T <= 32) and the LDS-tiled kernels, split over K while their tiles are few
+    (T = 33, 200, 700 ragged, 4096), against the oracle (every token up to 300, else
+    sampled tokens)."""
+    w, full, dev, x, _ = gpu_inputs("beam_dense_decode_t16", T, weight_dtype=dt)
+    print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T}", flush=True)
+    cfg = dense_cfg(w)
+    y = bm.beam_dense_forward(cfg, to_dev_x(w, x), dev["w13"], dev["w2"], w13_scale=dev.get("w13_scale"),
+                              w2_scale=dev.get("w2_scale"))
+    torch.cuda.synchronize()
+    tok = np.arange(T) if T <= 300 else sample_tokens(T)
+    ref = oracle.dense_forward(x_f32(w, x), dense_bank(w, full), token_subset=tok)
+    got = y.float().cpu().numpy()[tok].astype(np.float64)
+    err = rel_inf(got, ref["y"])
+    print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T} rel_inf={err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,T", [(DT_BF16, 300), (DT_FP8, 16)])
+def test_dense_sublayer(dt, T):
+    """pre-norm -> dense MLP -> post-norm -> residual, h updated in place."""
+    w, full, dev, x, _ = gpu_inputs("beam_dense_decode_t16", T, weight_dtype=dt, x_recipe="normal")
+    print(f"[case] dense sublayer {DTYPE_NAMES[dt]} T={T}", flush=True)
+    cfg = dense_cfg(w)
+    rs = np.random.default_rng(11)
+    g1 = (1 + 0.1 * rs.standard_normal(w.H)).astype(np.float32)
+    g2 = (1 + 0.1 * rs.standard_normal(w.H)).astype(np.float32)
+    h = to_dev_x(w, x)
+    out = torch.empty_like(h)
+    bm.beam_dense_sublayer_forward(cfg, h, w.step_k, dev["w13"], dev["w2"], pre_gain=torch.from_numpy(g1).cuda(),
+                                   post_gain=torch.from_numpy(g2).cuda(), w13_scale=dev.get("w13_scale"),
+                                   w2_scale=dev.get("w2_scale"), mlp_out=out)
+    torch.cuda.synchronize()
+    ref = oracle.dense_sublayer_forward(oracle.bf16_to_f32(x), g1, g2, w.step_k, w.norm_eps, dense_bank(w, full))
+    e_y = rel_inf(out.float().cpu().numpy().astype(np.float64), ref["y"])
+    e_h = rel_inf(h.float().cpu().numpy().astype(np.float64), ref["h_new"])
+    print(f"[case] dense sublayer {DTYPE_NAMES[dt]} T={T} mlp rel_inf={e_y:.3e} h rel_inf={e_h:.3e}", flush=True)
+    assert e_y <= TOL[dt] and e_h <= TOL[dt]
