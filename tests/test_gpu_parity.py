@@ -382,3 +382,48 @@ def test_dense_sublayer(dt, T):
     e_h = rel_inf(h.float().cpu().numpy().astype(np.float64), ref["h_new"])
     print(f"[case] dense sublayer {DTYPE_NAMES[dt]} T={T} mlp rel_inf={e_y:.3e} h rel_inf={e_h:.3e}", flush=True)
     assert e_y <= TOL[dt] and e_h <= TOL[dt]
+
+
+# ---------------------------------------------------------------------------
+# limits of the configuration and degenerate routing
+# ---------------------------------------------------------------------------
+_EDGE = {
+    # largest hidden size and top-k the kernels accept (H = 16384, K = 32)
+    "max_hidden_topk": dict(H=16384, I=128, E=64, G=8, Kg=4, K=32),
+    # one group: plain top-K over all experts
+    "single_group": dict(H=512, I=256, E=64, G=1, Kg=1, K=6),
+    # every group kept
+    "all_groups_kept": dict(H=256, I=128, E=32, G=4, Kg=4, K=8),
+    # K = 1: the weight is alpha exactly
+    "k1": dict(H=128, I=64, E=16, G=4, Kg=2, K=1, act_dtype=DT_F32, weight_dtype=DT_F32),
+    # the fewest experts: both picked
+    "two_experts": dict(H=128, I=64, E=2, G=1, Kg=1, K=2, act_dtype=DT_F32, weight_dtype=DT_F32),
+}
+
+
+@pytest.mark.parametrize("case,T", [("max_hidden_topk", 16), ("max_hidden_topk", 300), ("single_group", 100),
+                                    ("single_group", 700), ("all_groups_kept", 64), ("k1", 50),
+                                    ("two_experts", 40)])
+def test_config_limits_and_degenerate_routing(case, T):
+    from beam_inputs import Workload, make_inputs
+    w = Workload(f"edge_{case}", T=T, seed=3, x_recipe="rms_normal", **_EDGE[case])
+    print(f"[case] edge {case} T={T}", flush=True)
+    full = make_inputs(w)
+    dev = {"w_router": torch.from_numpy(full.w_router).cuda()}
+    if w.weight_dtype == DT_BF16:
+        dev["w13"] = torch.from_numpy(full.w13.view(np.int16)).cuda().view(torch.bfloat16)
+        dev["w2"] = torch.from_numpy(full.w2.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        dev["w13"] = torch.from_numpy(full.w13).cuda()
+        dev["w2"] = torch.from_numpy(full.w2).cuda()
+    cfg, y, ids, wts, ws = run_forward(w, dev, full.x, None)
+    ref = oracle.moe_forward(x_f32(w, full.x), full.w_router, None, bank_of(w, full), w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids, wts, ref["ids"], ref["w"])
+    check_permutation(w, ws, ids)
+    if w.K == 1:
+        assert (wts == np.float32(w.alpha)).all()
+    if w.K == w.E:
+        assert (np.sort(ids, axis=1) == np.arange(w.E)).all()
+    err = rel_inf(y.float().cpu().numpy().astype(np.float64), ref["y"])
+    print(f"[case] edge {case} T={T} rel_inf={err:.3e}", flush=True)
+    assert err <= TOL[w.weight_dtype]
