@@ -502,13 +502,15 @@ void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, cons
             else router_logits_tiled<false, 64, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
         }
     } else {
-        dim3 grid((T + 31) / 32, E / 128);
+        // 64 x 64 tiles (4 x 4 per thread): half the LDS reads per fma of 32 x 128 tiles
+        // at the same block count
+        dim3 grid((T + 63) / 64, E / 64);
         if (ch % 80 == 0) {
-            if (x_bf16) router_logits_tiled<true, 32, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
-            else router_logits_tiled<false, 32, 128, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            if (x_bf16) router_logits_tiled<true, 64, 64, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 64, 64, 80><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
         } else {
-            if (x_bf16) router_logits_tiled<true, 32, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
-            else router_logits_tiled<false, 32, 128, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            if (x_bf16) router_logits_tiled<true, 64, 64, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
+            else router_logits_tiled<false, 64, 64, 16><<<grid, 256, 0, st>>>(T, H, E, x, wr, bias, z);
         }
     }
 }

@@ -398,12 +398,14 @@ _EDGE = {
     "k1": dict(H=128, I=64, E=16, G=4, Kg=2, K=1, act_dtype=DT_F32, weight_dtype=DT_F32),
     # the fewest experts: both picked
     "two_experts": dict(H=128, I=64, E=2, G=1, Kg=1, K=2, act_dtype=DT_F32, weight_dtype=DT_F32),
+    # register-tiled router logits with 16-deep tiles (chunks of 16 hidden entries)
+    "short_chunks": dict(H=1024, I=256, E=128, G=8, Kg=4, K=8),
 }
 
 
 @pytest.mark.parametrize("case,T", [("max_hidden_topk", 16), ("max_hidden_topk", 300), ("single_group", 100),
                                     ("single_group", 700), ("all_groups_kept", 64), ("k1", 50),
-                                    ("two_experts", 40)])
+                                    ("two_experts", 40), ("short_chunks", 4096), ("short_chunks", 16384)])
 def test_config_limits_and_degenerate_routing(case, T):
     from beam_inputs import Workload, make_inputs
     w = Workload(f"edge_{case}", T=T, seed=3, x_recipe="rms_normal", **_EDGE[case])
@@ -417,13 +419,18 @@ def test_config_limits_and_degenerate_routing(case, T):
         dev["w13"] = torch.from_numpy(full.w13).cuda()
         dev["w2"] = torch.from_numpy(full.w2).cuda()
     cfg, y, ids, wts, ws = run_forward(w, dev, full.x, None)
-    ref = oracle.moe_forward(x_f32(w, full.x), full.w_router, None, bank_of(w, full), w.G, w.Kg, w.K, w.alpha)
+    tok = np.arange(T) if T <= 1000 else sample_tokens(T)
+    ref = oracle.moe_forward(x_f32(w, full.x), full.w_router, None, bank_of(w, full), w.G, w.Kg, w.K, w.alpha,
+                             token_subset=tok)
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    z = ws_region(ws, m["logits"], w.T * w.E, np.float32).reshape(w.T, w.E)
+    assert np.array_equal(z, ref["logits"])            # logits bit for bit
     check_routing(w, ids, wts, ref["ids"], ref["w"])
     check_permutation(w, ws, ids)
     if w.K == 1:
         assert (wts == np.float32(w.alpha)).all()
     if w.K == w.E:
         assert (np.sort(ids, axis=1) == np.arange(w.E)).all()
-    err = rel_inf(y.float().cpu().numpy().astype(np.float64), ref["y"])
+    err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
     print(f"[case] edge {case} T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[w.weight_dtype]
