@@ -238,6 +238,18 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     return g;
 }
 
+// LDS-tiled GEMMs.  The 128-byte-stage kernel (gemm_wide.hip) for BF16 weights streamed
+// with few rows per expert (tile pairs, the weight-bound regime; its operands addressed
+// with 32-bit offsets), the 64-byte-stage kernel otherwise: with FP8 or MXFP4 weights
+// and where many rows share each weight panel it is the faster one (measured).
+// a_rows: rows of the activation matrix.
+int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt, int64_t a_rows) {
+    const int64_t nw = (mode == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
+    const bool fits = a_rows * g.lda * 2 < (int64_t{1} << 32) && nw * g.kd * 2 < (int64_t{1} << 32);
+    if (wt == PrefillWeights::kBf16 && g.group_m == 2 && fits) return launch_gemm_wide(st, mode, g);
+    return launch_gemm_prefill(st, mode, g, wt);
+}
+
 // Expert GEMMs: x_exp [T, H] in the weights' activation format -> down_out [T*K, H]
 // (yperm for the MoE layer).  dense: the single weight set of the dense MLP (rows are
 // tokens, no gather), whose streaming down GEMM may split K into FP32 partial sums that
@@ -280,20 +292,20 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) slices1 = launch_gemm_bf16_decode(st, kGateUp, g1);
-            else slices1 = launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kBf16);
+            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kBf16, T);
         }
         swiglu();
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) slices = launch_gemm_bf16_decode(st, kDown, g2);
-            else slices = launch_gemm_prefill(st, kDown, g2, PrefillWeights::kBf16);
+            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kBf16, P);
         }
     } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) slices1 = launch_gemm_fp8_decode(st, kGateUp, g1);
-            else slices1 = launch_gemm_prefill(st, kGateUp, g1, PrefillWeights::kFp8);
+            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kFp8, T);
         }
         swiglu();
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
@@ -301,7 +313,7 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) slices = launch_gemm_fp8_decode(st, kDown, g2);
-            else slices = launch_gemm_prefill(st, kDown, g2, PrefillWeights::kFp8);
+            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kFp8, P);
         }
     } else {            // MXFP4 weights
         {

@@ -1,0 +1,332 @@
+// Grouped expert GEMMs for many rows per expert with BF16 weights: LDS-tiled MFMA GEMM
+// whose K stages hold 128 bytes of every operand row.
+//
+// SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
+// routed per token"; FP32 SwiGLU product per the "Residual stream" section):
+//   gate/up:  h[r, j] = SiLU(a_r . Wg[j]) * (a_r . Wu[j])   (a_r gathered by token)
+//   down:     y[r, n] = h_r . Wd[n]
+// Tiles, wave roles, MFMAs, epilogue and block order are those of the 64-byte-stage
+// kernel in gemm_prefill.hip (which serves the other cases): 256 x 256 output
+// tiles of one expert, 4 waves of 128 x 128 as 4 x 4 MFMA tiles of 32 x 32, gate and up
+// rows of the same columns in one tile so the SwiGLU is applied in registers.
+//
+// Why 128-byte stages: a direct global->LDS load moves 16 bytes per lane; with 64-byte
+// row pieces every request covers half an L2 line, and measured on gfx950 the L2 then
+// delivers 16-19 TB/s to LDS against 30-32 TB/s for 128-byte row pieces (panels
+// resident in L2), which is what bounds the 64-byte-stage kernel where activation tiles
+// and shared weight panels come from L2.  A stage is 32 KB of activations (256 rows x
+// 128 bytes) and 32 KB of weights; the 160 KB of LDS hold two activation slots and three
+// weight slots, so while stage j is computed the activations of stage j + 1 and the
+// weights of stages j + 1 and j + 2 (the HBM stream) are in flight.  (Measured on the
+// Beam layer it beats the 64-byte-stage kernel where BF16 weights stream from HBM with
+// few rows per expert -- 4096 tokens: gate/up 2.65 against 2.83 ms, down 1.49 against
+// 1.60 -- and loses where many rows share each weight panel; a version of it for FP8
+// weights lost at 8192 tokens, 3.01 against 2.73 ms.)
+#include "common.cuh"
+#include "kernels.h"
+
+namespace beam {
+
+namespace {
+constexpr int kWideRowBytes = 128;               // K bytes of an operand row per stage
+constexpr int kWideOpBytes = 256 * kWideRowBytes;     // one operand (256 rows) of one stage
+constexpr int kWideASlots = 2, kWideBSlots = 3;
+constexpr size_t kWideLds = (kWideASlots + kWideBSlots) * static_cast<size_t>(kWideOpBytes);
+static_assert(kWideLds <= 160 * 1024, "LDS budget");
+
+// 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7): the 16 consecutive rows one
+// fragment read serves per LDS cycle (same chunk) fill both halves of the 256-byte bank
+// period with 8 distinct slots each, i.e. all 64 banks.
+__device__ __forceinline__ int wide_offset(int row, int chunk) {
+    return row * kWideRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Byte offset inside a row's 128-byte K piece of the chunk lane `lane` moves in a DMA
+// instruction covering rows base .. base + 7 (base a multiple of 8, `odd` = bit 3 of
+// base): lane i lands in row base + i / 8, slot i % 8.
+__device__ __forceinline__ int wide_dma_chunk(int lane, int odd) {
+    return ((lane & 7) ^ (((lane >> 4) + 4 * odd) & 7)) << 4;
+}
+
+// Fragments of one MFMA K step (16 K values, 8 per lane) for one wave.
+struct StepFrags { bf16x8 a[4]; bf16x8 b[4]; };
+}  // namespace
+
+// Pipeline per stage kt (KS = 4 MFMA K steps of 16), fragments double
+// buffered in registers: K steps 0 .. KS-2 run their MFMAs while reading the next step's
+// fragments from the stage's slots; before the last step every wave waits until stage
+// kt + 1 has landed (only the weight loads of stage kt + 2 may still be in flight) and
+// meets the others, then loads the activations of stage kt + 2 and the weights of stage
+// kt + 3 into the slots stage kt drained, runs the last step's MFMAs and reads stage
+// kt + 1's first fragments.
+//
+// SPLIT: as in gemm_prefill.hip, the GEMMs of a single weight set split K into
+// g.k_slices slices (FP32 partial sums) over a flat block order.
+template <int MODE, bool GATHER, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
+    constexpr int BM = kPrefillBM, BN = 256, MI = 4, NI = 4;
+    constexpr int EB = 2;                               // bytes per element (A and B)
+    constexpr int BK = kWideRowBytes / EB;              // K per stage
+    constexpr int KS = 4;                               // MFMA K steps per stage
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
+    const int n_tiles_n = g.n_out / NCOL;
+    int tile, nt, kz = 0;
+    if constexpr (SPLIT) {
+        const int lin = blockIdx.x;
+        kz = lin % g.k_slices;
+        const int rest = lin / g.k_slices;
+        nt = rest % n_tiles_n;
+        tile = rest / n_tiles_n;
+    } else {
+        prefill_tile_of_block(n_tiles_n, g.group_m, tile, nt);
+    }
+    if (tile >= g.meta[kMetaTiles]) return;
+    const int2 ti = g.tiles[tile];                     // (expert, tile of the expert)
+    const int e = ti.x, n_e = g.exp_cnt[e];
+    const int first = expert_tile_first(n_e, ti.y, BM);
+    const int rows = expert_tile_first(n_e, ti.y + 1, BM) - first;
+    const int row0 = g.exp_off[e] + first;
+    const int c0 = nt * NCOL;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
+    const int64_t krow = static_cast<int64_t>(g.kd) * EB;        // bytes per weight row
+    const int klen = SPLIT ? g.kd / g.k_slices : g.kd;           // K slice of this block
+    const int kbeg = SPLIT ? kz * klen : 0;
+
+    // MFMA row tiles of this wave that hold rows of the expert (wave-uniform; a prefix of
+    // the wave's tiles): the others skip their loads, LDS reads and MFMAs.
+    const int ntiles = (rows + 31) / 32;
+    const int mvalid = __builtin_amdgcn_readfirstlane(min(MI, max(0, (ntiles - wm + 1) / 2)));
+
+    // Direct-to-LDS assignment, 8 rows x 128 bytes per wave instruction.  A: wave (wm, wn)
+    // moves rows (wm + 2 i) * 32 + 16 wn + 8 h + lane / 8 (h < 2) of each of its live row
+    // tiles i, the rows the pair (wm, 0), (wm, 1) reads; rows past the expert's end
+    // re-load its last row (never read back).  B: wave w moves rows w * 64 + 8 j + lane / 8
+    // (j < 8; for gate/up waves 0-1 move gate rows, 2-3 up rows).
+    // Addresses are block-uniform bases plus 32-bit lane offsets (the launcher checks
+    // that the activation rows span less than 4 GB; one expert's weights always do).
+    const int dr = lane >> 3;
+    const uint8_t* abase = static_cast<const uint8_t*>(g.a) + static_cast<int64_t>(kbeg) * EB;
+    uint32_t aoff[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rr = min((wm + 2 * i) * 32 + 16 * wn + 8 * h + dr, rows - 1);
+            const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
+            aoff[i][h] = static_cast<uint32_t>(arow * g.lda * EB) + wide_dma_chunk(lane, h);
+        }
+    auto weight_row = [&](int r) -> int {                // block row r (0..255) -> weight row
+        if (MODE == kGateUp) return (r < BN / 2) ? c0 + r : g.n_out + c0 + (r - BN / 2);
+        return c0 + r;
+    };
+    const uint8_t* bbase = static_cast<const uint8_t*>(g.w) + static_cast<int64_t>(e) * nw * krow +
+                           static_cast<int64_t>(kbeg) * EB;
+    const uint32_t boff = static_cast<uint32_t>(weight_row(wave * 64 + dr) * krow);
+    const uint32_t bch0 = wide_dma_chunk(lane, 0), bch1 = wide_dma_chunk(lane, 1);
+    const uint32_t bstep = static_cast<uint32_t>(8 * krow);   // bytes between B rows j and j + 1
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+    const int l32 = lane & 31, lh = lane >> 5;
+    int arow_l[MI], brow_l[NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) arow_l[i] = (wm + 2 * i) * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
+                                      : wn * 128 + i * 32 + l32;
+    }
+    const int nk = klen / BK;          // slices are multiples of BK
+
+    auto k_loop = [&](auto mv_tag) {
+        constexpr int MV = decltype(mv_tag)::value;
+        constexpr int PER = 2 * MV + 8;                 // direct-to-LDS loads per stage and wave
+        constexpr int NM = MV * NI;                      // MFMAs per K step
+        constexpr int NR = MV == 0 ? 0 : MV + NI;        // LDS reads per K step
+        auto dma_a = [&](int slot, int kt) {            // activations of stage kt
+            uint8_t* As = smem + slot * kWideOpBytes;
+            const uint8_t* ak = abase + static_cast<int64_t>(kt) * kWideRowBytes;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                if (i < MV) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        lds_dma16(ak + aoff[i][h], As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kWideRowBytes);
+                }
+        };
+        auto dma_b = [&](int slot, int kt) {            // weights of stage kt (8 loads)
+            uint8_t* Bs = smem + (kWideASlots + slot) * kWideOpBytes;
+            const uint8_t* bk = bbase + static_cast<int64_t>(kt) * kWideRowBytes;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                lds_dma16(bk + (boff + j * bstep + ((j & 1) ? bch1 : bch0)), Bs + (wave * 64 + 8 * j) * kWideRowBytes);
+        };
+        auto rd = [&](const uint8_t* T, int row, int c) {
+            return *reinterpret_cast<const u32x4*>(T + wide_offset(row, c));
+        };
+        // fragments of K step s of a stage whose operands are in slots aslot, bslot
+        auto load_frags = [&](StepFrags& f, int aslot, int bslot, int s) {
+            const uint8_t* As = smem + aslot * kWideOpBytes;
+            const uint8_t* Bs = smem + (kWideASlots + bslot) * kWideOpBytes;
+            // 16 bytes per lane: K values 16 s + 8 lh .. + 7 = chunk 2 s + lh
+            const int c = 2 * s + lh;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                if (mi < MV) f.a[mi] = __builtin_bit_cast(bf16x8, rd(As, arow_l[mi], c));
+            if (MV > 0) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) f.b[ni] = __builtin_bit_cast(bf16x8, rd(Bs, brow_l[ni], c));
+            }
+        };
+        auto mfma_step = [&](const StepFrags& f) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                if (mi < MV) {
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+                }
+        };
+
+        StepFrags f0, f1;
+        // prologue: A0 B0 A1 B1 B2 in this order; wait for stage 0 (A0, B0)
+        dma_a(0, 0);
+        dma_b(0, 0);
+        if (nk > 1) {
+            dma_a(1, 1);
+            dma_b(1, 1);
+        }
+        if (nk > 2) dma_b(2, 2);
+        if (nk > 2) wait_lds_dma<2 * MV + 16>();
+        else if (nk > 1) wait_lds_dma<2 * MV + 8>();
+        else wait_lds_dma<0>();
+        lds_pipeline_barrier();
+        load_frags(f0, 0, 0, 0);
+        int bslot = 0;                                   // weight slot of stage kt (kt % 3)
+        for (int kt = 0; kt < nk; ++kt) {
+            const int aslot = kt & 1;
+            const int bnext = (bslot == kWideBSlots - 1) ? 0 : bslot + 1;
+            // K steps 0 .. KS-2 (KS is even, so the buffers alternate statically)
+#pragma unroll
+            for (int s = 0; s + 1 < KS; ++s) {
+                StepFrags& cur = (s & 1) ? f1 : f0;
+                StepFrags& nxt = (s & 1) ? f0 : f1;
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_step(cur);
+                load_frags(nxt, aslot, bslot, s + 1);
+                sched_interleave<NM, NR, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // last K step.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has
+            // landed once at most the 8 weight loads of stage kt + 2 are in flight.
+            if (kt + 2 < nk) wait_lds_dma<8>();
+            else wait_lds_dma<0>();
+            lds_pipeline_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(f1);
+            if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
+            if (kt + 2 < nk) dma_a(aslot, kt + 2);        // into the slots stage kt drained
+            if (kt + 3 < nk) dma_b(bslot, kt + 3);
+            sched_interleave<NM, NR, PER>();
+            __builtin_amdgcn_sched_barrier(0);
+            bslot = bnext;
+        }
+    };
+    dispatch_row_tiles<MI>(mvalid, k_loop);
+
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = (wm + 2 * mi) * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            if (m >= rows) continue;
+            constexpr float sa = 1.0f;
+            uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
+            if constexpr (SPLIT) {
+                // FP32 partial sums of the slice: gate then up sums for gate/up (the SwiGLU
+                // follows the reduction)
+                float* prow = g.part + kz * g.part_slice +
+                              static_cast<int64_t>(row0 + m) * (MODE == kGateUp ? 2 * g.n_out : g.ldo);
+                if (MODE == kGateUp) {
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        prow[c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni][i] * sa;
+                        prow[g.n_out + c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni + 2][i] * sa;
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) prow[c0 + wn * 128 + ni * 32 + l32] = acc[mi][ni][i] * sa;
+                }
+                continue;
+            }
+            if (MODE == kGateUp) {
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    orow[c0 + wn * 64 + ni * 32 + l32] =
+                        f32_to_bf16_bits(silu(acc[mi][ni][i] * sa) * (acc[mi][ni + 2][i] * sa));
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
+            }
+        }
+    }
+}
+
+template <int MODE, bool GATHER, bool SPLIT>
+static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
+    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, SPLIT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kWideLds));
+        attr_set = true;
+    }
+    const size_t lds = kWideLds;
+    if (SPLIT) {
+        GroupedGemmArgs gs = g;
+        gs.k_slices = ks;
+        gemm_wide<MODE, GATHER, SPLIT><<<blocks, 256, lds, st>>>(gs);
+    } else {
+        gemm_wide<MODE, GATHER, SPLIT><<<blocks, 256, lds, st>>>(g);
+    }
+}
+
+static void launch_wide_modes(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks, int ks) {
+    // split K only for a single weight set (rows in token order, no gather); the grid
+    // enumerates every (row tile bound, column tile, slice)
+    if (ks > 1) {
+        const int ncol = (mode == kGateUp) ? 128 : 256;
+        const int nb = g.max_tiles * (g.n_out / ncol) * ks;
+        if (mode == kGateUp) launch_wide_inst<kGateUp, false, true>(st, g, nb, ks);
+        else launch_wide_inst<kDown, false, true>(st, g, nb, ks);
+    } else if (mode == kGateUp) {
+        if (g.gather) launch_wide_inst<kGateUp, true, false>(st, g, blocks, 1);
+        else launch_wide_inst<kGateUp, false, false>(st, g, blocks, 1);
+    } else {
+        if (g.gather) launch_wide_inst<kDown, true, false>(st, g, blocks, 1);
+        else launch_wide_inst<kDown, false, false>(st, g, blocks, 1);
+    }
+}
+
+int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+    if (g.max_tiles == 0) return 1;
+    const int ncol = (mode == kGateUp) ? 128 : 256;
+    // every (row tile, column tile) of whole groups of group_m row tiles, in whole XCD chunks
+    const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
+    const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
+    const int ks = prefill_k_split(mode, g, PrefillWeights::kBf16);
+    launch_wide_modes(st, mode, g, blocks, ks);
+    return ks;
+}
+
+}  // namespace beam

@@ -12,8 +12,6 @@ constexpr int kMetaTiles = 0;       // meta[0]: number of (expert, row-tile) til
 constexpr int kMetaActive = 1;      // meta[1]: number of experts with >= 1 row
 constexpr int kMetaInts = 64;
 
-// Rows per tile of the prefill grouped GEMMs: 256, or 128 when the average expert has
-// fewer than ~192 rows (less padding where the GEMM is bound by streaming weights).
 constexpr int kPrefillBM = 256;     // rows per tile of the prefill grouped GEMMs
 // Tiles of an expert with n routed rows for the prefill GEMMs: ceil(n / BM) tiles of
 // whole 32-row blocks, as equal as possible (so the tiles of one expert carry the same
@@ -123,6 +121,8 @@ constexpr int kFp8PrefillMaxKd = 32768;     // LDS holds the K-block scale codes
 // prefill_k_split gives beforehand.  MXFP4 slices hold at most kMxfp4PrefillMaxKd of K.
 int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
 int prefill_k_split(GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
+// gemm_wide.hip: the same GEMMs for BF16 weights with 128-byte K stages
+int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
 
 // elementwise.hip
 void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,
