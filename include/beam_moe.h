@@ -212,8 +212,8 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
  * norm_eps finite and >= 0, else BEAM_ERR_INVALID_ARG); the router fields are ignored.
  * Kernel support is that of the MoE layer's expert GEMMs (dtype pairs, multiples and
  * per-call limits above), except that the streaming kernels, which read the weights
- * once per 32 rows, serve up to 32 tokens and the LDS-tiled kernels above, and that
- * above 32 tokens MXFP4 weights need hidden <= 8192 and inter a multiple of 512 s, s
+ * once per 32 rows, serve up to 16 tokens and the LDS-tiled kernels above, and that
+ * above 16 tokens MXFP4 weights need hidden <= 8192 and inter a multiple of 512 s, s
  * the least power of two with inter / s <= 8192 (s <= 16).  While the tiles are few
  * both GEMMs split the reduction into slices whose FP32 partial sums the workspace
  * holds.  The weights have the layout of one expert of beam_moe_forward (E = 1):

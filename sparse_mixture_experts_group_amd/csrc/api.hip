@@ -268,10 +268,11 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
     g2.lda = I; g2.gather = false;
     g2.w = w2; g2.w_scale = w2_scale; g2.n_out = H; g2.kd = I;
     g2.out = down_out; g2.ldo = H;
-    // streaming kernels while the rows of an expert are few: T tokens spread over the
-    // experts, or at most 32 rows of the dense MLP's single weight set (the streaming
-    // kernels read the weights once per 32 rows)
-    const bool decode = dense ? T <= kDenseStreamMaxT : T <= kDecodeMaxT;
+    // streaming kernels while the rows of an expert are few (measured crossovers): T
+    // tokens spread over the experts, or at most 16 rows of the dense MLP's single weight
+    // set (the streaming kernels read the weights once per 32 rows)
+    const bool decode = dense ? T <= kDenseStreamMaxT
+                              : T <= (c.weight_dtype == BEAM_DTYPE_BF16 ? kBf16StreamMaxT : kDecodeMaxT);
     if (dense && c.weight_dtype != BEAM_DTYPE_F32) {
         g1.part = g2.part = at<float>(ws, L.part);
         g1.part_cap = g2.part_cap = dense_part_floats(c, T);

@@ -179,7 +179,7 @@ def test_dense_argument_errors_before_any_launch():
     assert fwd(16, FAKE, FAKE, FAKE, 1 << 40, s13=FAKE) == bm.BEAM_ERR_INVALID_ARG
     need = bm.beam_dense_workspace_size(c, 16)
     assert fwd(16, FAKE, FAKE, FAKE, need - 1) == bm.BEAM_ERR_WORKSPACE
-    # MXFP4 above the dense streaming range (32 tokens): the tiled kernels stage a K
+    # MXFP4 above the dense streaming range (16 tokens): the tiled kernels stage a K
     # slice's weight scales in LDS (at most 8192 long), so the down GEMM of width 20480
     # runs in 4 slices; hidden must stay <= 8192 and the width split into whole slices
     c4 = bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4)
@@ -190,7 +190,7 @@ def test_dense_argument_errors_before_any_launch():
         bm.BEAM_ERR_UNSUPPORTED
     assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, inter=20608), 33, 1 << 40) == \
         bm.BEAM_ERR_UNSUPPORTED
-    assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, inter=20608), 32, 16) == \
+    assert mx(bm.make_dense_config(weight_dtype=bm.BEAM_DTYPE_MXFP4, inter=20608), 16, 16) == \
         bm.BEAM_ERR_WORKSPACE
     sub = lambda cfg, k, nb: L.beam_dense_sublayer_forward(ctypes.byref(cfg), 16, FAKE, None, None, k, FAKE,
                                                            None, FAKE, None, None, FAKE, nb, None)

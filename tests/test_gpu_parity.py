@@ -192,7 +192,8 @@ def test_router_all_ties_and_duplicated_columns():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,T", [("beam_decode_t16", None), ("beam_decode_t16", 1),
                                     ("beam_decode_t16", 17), ("beam_decode_t16", 32),
-                                    ("beam_prefill_t4096", 33), ("beam_prefill_t4096", 256),
+                                    ("beam_prefill_t4096", 33), ("beam_prefill_t4096", 127),
+                                    ("beam_prefill_t4096", 128), ("beam_prefill_t4096", 256),
                                     ("beam_prefill_t4096", 257), ("beam_prefill_t4096", 1000),
                                     ("beam_prefill_t4096", None),
                                     ("beam_prefill_t4096", 4097), ("beam_skewed_t32768", None)])
@@ -339,13 +340,13 @@ def dense_cfg(w):
                                 fp8_block=w.fp8_block, norm_eps=w.norm_eps)
 
 
-@pytest.mark.parametrize("dt,T", [(DT_BF16, 16), (DT_BF16, 1), (DT_BF16, 32), (DT_BF16, 33), (DT_BF16, 200),
+@pytest.mark.parametrize("dt,T", [(DT_BF16, 16), (DT_BF16, 1), (DT_BF16, 17), (DT_BF16, 32), (DT_BF16, 33), (DT_BF16, 200),
                                   (DT_BF16, 700), (DT_BF16, 4096), (DT_FP8, 16), (DT_FP8, 200), (DT_FP8, 700),
                                   (DT_MXFP4, 16), (DT_MXFP4, 32), (DT_MXFP4, 200), (DT_MXFP4, 4096)])
 def test_dense_forward(dt, T):
     """Dense MLP through beam_dense_forward: streaming kernels with both GEMMs split
-    over K (T <= 32) and the LDS-tiled kernels, split over K while their tiles are few
-    (T = 33, 200, 700 ragged, 4096), against the oracle (every token up to 300, else
+    over K (T <= 16) and the LDS-tiled kernels, split over K while their tiles are few
+    (T = 32, 33, 200, 700 ragged, 4096), against the oracle (every token up to 300, else
     sampled tokens)."""
     w, full, dev, x, _ = gpu_inputs("beam_dense_decode_t16", T, weight_dtype=dt)
     print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T}", flush=True)
