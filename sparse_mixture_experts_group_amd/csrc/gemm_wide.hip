@@ -232,11 +232,18 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             else wait_lds_dma<0>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            mfma_step(f1);
-            if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
             if (kt + 2 < nk) dma_a(aslot, kt + 2);        // into the slots stage kt drained
             if (kt + 3 < nk) dma_b(bslot, kt + 3);
-            sched_interleave<NM, NR, PER>();
+            mfma_step(f1);
+            if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
+            // the loads first (two after each of the first MFMAs; PER is even), then the
+            // fragment reads of stage kt + 1
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+                if (2 * i < PER) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // VMEM
+                else if (i - PER / 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
             __builtin_amdgcn_sched_barrier(0);
             bslot = bnext;
         }
