@@ -82,9 +82,10 @@ struct GroupedGemmArgs {
     int max_rows;             // bound on the rows of one expert (min(T, T*K))
     void* out;                // [rows, n_out]
     int64_t ldo;              // elements per output row
-    // Streaming GEMMs only: when non-null the launcher may split K over blockIdx.z (for a
-    // single weight set, whose GEMMs alone have too few column blocks to fill the chip);
-    // slice z then writes FP32 partial sums to part + z * part_slice instead of out: rows
+    // When non-null the launcher may split K (for a single weight set, whose GEMMs alone
+    // have too few blocks to fill the chip; streaming kernels over blockIdx.z, tiled ones
+    // over a flat block order); slice z then writes FP32 partial sums to
+    // part + z * part_slice instead of out: rows
     // of n_out sums for down, of 2 n_out for gate/up (gate sums, then up sums; the SwiGLU
     // is applied after the reduction).  part_cap bounds the floats of all slices.  The
     // launcher returns the slice count.
@@ -95,10 +96,11 @@ struct GroupedGemmArgs {
 };
 constexpr int kMaxKSplit = 16;
 
-// K slices for a streaming GEMM of `blocks` column blocks whose partial sums take
-// `out_elems` floats per slice: doubled while the grid holds fewer than four blocks per
-// CU, every slice stays a multiple of `step` (the kernel's widest K step) and the slices
-// fit in `cap` floats.
+// K slices for a GEMM of a single weight set with `blocks` blocks (column blocks of the
+// streaming kernels, tiles of the LDS-tiled ones) whose partial sums take `out_elems`
+// floats per slice: doubled while the grid holds fewer than four blocks per CU, every
+// slice stays a multiple of `step` (the kernel's widest K step) and the slices fit in
+// `cap` floats.
 inline int decode_k_split(int64_t blocks, int kd, int step, int64_t out_elems, int64_t cap) {
     int s = 1;
     while (s < kMaxKSplit && blocks * s < 1024 && kd % (2 * s * step) == 0 && 2 * s * out_elems <= cap) s *= 2;
