@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbeam_moe.so")
-SOURCES = ["api.hip", "router.hip", "gemm_f32.hip", "gemm_bf16_decode.hip", "gemm_prefill.hip", "gemm_wide.hip",
+SOURCES = ["api.hip", "router.hip", "gemm_f32.hip", "gemm_bf16_decode.hip", "gemm_prefill.hip", "gemm_wide.hip", "gemm_wide_mx.hip",
            "gemm_fp8.hip", "gemm_mxfp4.hip", "elementwise.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -126,6 +126,10 @@ int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g,
 int prefill_k_split(GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
 // gemm_wide.hip: the same GEMMs for BF16 weights with 128-byte K stages
 int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// gemm_wide_mx.hip: the same for MXFP4 weights with 128-value K stages, for K slices of at
+// most 6144 (wide_mx_supported); ks = prefill_k_split(mode, g, kMxfp4)
+bool wide_mx_supported(const GroupedGemmArgs& g, int ks);
+int launch_gemm_wide_mx(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int ks);
 
 // elementwise.hip
 void launch_combine(hipStream_t st, int64_t T, int H, int K, bool f32, const void* yperm,
