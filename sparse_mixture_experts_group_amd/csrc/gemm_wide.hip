@@ -1,5 +1,6 @@
-// Grouped expert GEMMs for many rows per expert with BF16 weights: LDS-tiled MFMA GEMM
-// whose K stages hold 128 bytes of every operand row.
+// Grouped expert GEMMs for many rows per expert with BF16 or FP8 (OCP E4M3FN, 128 x 128
+// power-of-two block scales, E4M3 activations with row scales) weights: LDS-tiled MFMA
+// GEMM whose K stages hold 128 bytes of every operand row.
 //
 // SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
 // routed per token"; FP32 SwiGLU product per the "Residual stream" section):
@@ -20,8 +21,8 @@
 // weights of stages j + 1 and j + 2 (the HBM stream) are in flight.  (Measured on the
 // Beam layer it beats the 64-byte-stage kernel where BF16 weights stream from HBM with
 // few rows per expert -- 4096 tokens: gate/up 2.65 against 2.83 ms, down 1.49 against
-// 1.60 -- and loses where many rows share each weight panel; a version of it for FP8
-// weights lost at 8192 tokens, 3.01 against 2.73 ms.)
+// 1.60 -- and loses where all four row tiles of a wave are live, e.g. FP8 weights at
+// 8192 tokens, 3.01 against 2.73 ms.)
 #include "common.cuh"
 #include "kernels.h"
 
@@ -48,26 +49,39 @@ __device__ __forceinline__ int wide_dma_chunk(int lane, int odd) {
     return ((lane & 7) ^ (((lane >> 4) + 4 * odd) & 7)) << 4;
 }
 
-// Fragments of one MFMA K step (16 K values, 8 per lane) for one wave.
-struct StepFrags { bf16x8 a[4]; bf16x8 b[4]; };
+constexpr int kUnitScale = 0x7f;                 // E8M0 code of 2^0
+
+__device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Fragments of one MFMA K step for one wave: BF16 - 16 K values (8 per lane); FP8 - 64 K
+// values (32 per lane).
+template <bool FP8> struct StepFrags;
+template <> struct StepFrags<false> { bf16x8 a[4]; bf16x8 b[4]; };
+template <> struct StepFrags<true> { i32x8 a[4]; i32x8 b[4]; };
 }  // namespace
 
-// Pipeline per stage kt (KS = 4 MFMA K steps of 16), fragments double
+// Pipeline per stage kt (KS MFMA K steps: 4 of 16 for BF16, 2 of 64 for FP8), fragments double
 // buffered in registers: K steps 0 .. KS-2 run their MFMAs while reading the next step's
 // fragments from the stage's slots; before the last step every wave waits until stage
 // kt + 1 has landed (only the weight loads of stage kt + 2 may still be in flight) and
 // meets the others, then loads the activations of stage kt + 2 and the weights of stage
 // kt + 3 into the slots stage kt drained, runs the last step's MFMAs and reads stage
-// kt + 1's first fragments.
+// kt + 1's first fragments.  FP8: one 128 x 128 scale block per stage, at most 64 per
+// reduction (a lane of a register each).
 //
 // SPLIT: as in gemm_prefill.hip, the GEMMs of a single weight set split K into
 // g.k_slices slices (FP32 partial sums) over a flat block order.
-template <int MODE, bool GATHER, bool SPLIT>
+template <int MODE, bool GATHER, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     constexpr int BM = kPrefillBM, BN = 256, MI = 4, NI = 4;
-    constexpr int EB = 2;                               // bytes per element (A and B)
+    constexpr int EB = FP8 ? 1 : 2;                     // bytes per element (A and B)
     constexpr int BK = kWideRowBytes / EB;              // K per stage
-    constexpr int KS = 4;                               // MFMA K steps per stage
+    constexpr int KS = FP8 ? 2 : 4;                     // MFMA K steps per stage
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NCOL = (MODE == kGateUp) ? BN / 2 : BN;   // output columns per tile
     const int n_tiles_n = g.n_out / NCOL;
@@ -128,6 +142,27 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     const uint32_t bch0 = wide_dma_chunk(lane, 0), bch1 = wide_dma_chunk(lane, 1);
     const uint32_t bstep = static_cast<uint32_t>(8 * krow);   // bytes between B rows j and j + 1
 
+    // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l of the slice
+    // (gate-column block in s_lo, up-column block in s_hi for gate/up; this wave's column
+    // block for down).
+    int s_lo = kUnitScale, s_hi = kUnitScale;
+    if constexpr (FP8) {
+        const int kb_all = g.kd / 128, kb_n = klen / 128;
+        const float* wsc = static_cast<const float*>(g.w_scale) + kbeg / 128;
+        const float* r_lo;
+        const float* r_hi;
+        if (MODE == kGateUp) {
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + c0 / 128) * kb_all;
+            r_hi = wsc + (static_cast<int64_t>(e) * (nw / 128) + (g.n_out + c0) / 128) * kb_all;
+        } else {
+            r_lo = wsc + (static_cast<int64_t>(e) * (nw / 128) + (c0 + wn * 128) / 128) * kb_all;
+            r_hi = r_lo;
+        }
+        const int l = min(lane, kb_n - 1);
+        s_lo = (__float_as_uint(r_lo[l]) >> 23) & 0xff;
+        s_hi = (__float_as_uint(r_hi[l]) >> 23) & 0xff;
+    }
+
     f32x16 acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -151,7 +186,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         constexpr int MV = decltype(mv_tag)::value;
         constexpr int PER = 2 * MV + 8;                 // direct-to-LDS loads per stage and wave
         constexpr int NM = MV * NI;                      // MFMAs per K step
-        constexpr int NR = MV == 0 ? 0 : MV + NI;        // LDS reads per K step
+        constexpr int NR = MV == 0 ? 0 : (FP8 ? 2 : 1) * (MV + NI);   // LDS reads per K step
         auto dma_a = [&](int slot, int kt) {            // activations of stage kt
             uint8_t* As = smem + slot * kWideOpBytes;
             const uint8_t* ak = abase + static_cast<int64_t>(kt) * kWideRowBytes;
@@ -174,30 +209,59 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             return *reinterpret_cast<const u32x4*>(T + wide_offset(row, c));
         };
         // fragments of K step s of a stage whose operands are in slots aslot, bslot
-        auto load_frags = [&](StepFrags& f, int aslot, int bslot, int s) {
+        auto load_frags = [&](StepFrags<FP8>& f, int aslot, int bslot, int s) {
             const uint8_t* As = smem + aslot * kWideOpBytes;
             const uint8_t* Bs = smem + (kWideASlots + bslot) * kWideOpBytes;
-            // 16 bytes per lane: K values 16 s + 8 lh .. + 7 = chunk 2 s + lh
-            const int c = 2 * s + lh;
+            if constexpr (FP8) {
+                // 32 bytes per lane: K values 64 s + 32 lh .. + 31 = chunks 4 s + 2 lh, + 1
+                const int c = 4 * s + 2 * lh;
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                if (mi < MV) f.a[mi] = __builtin_bit_cast(bf16x8, rd(As, arow_l[mi], c));
-            if (MV > 0) {
+                for (int mi = 0; mi < MI; ++mi)
+                    if (mi < MV) f.a[mi] = join8(rd(As, arow_l[mi], c), rd(As, arow_l[mi], c + 1));
+                if (MV > 0) {
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) f.b[ni] = __builtin_bit_cast(bf16x8, rd(Bs, brow_l[ni], c));
+                    for (int ni = 0; ni < NI; ++ni) f.b[ni] = join8(rd(Bs, brow_l[ni], c), rd(Bs, brow_l[ni], c + 1));
+                }
+            } else {
+                // 16 bytes per lane: K values 16 s + 8 lh .. + 7 = chunk 2 s + lh
+                const int c = 2 * s + lh;
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    if (mi < MV) f.a[mi] = __builtin_bit_cast(bf16x8, rd(As, arow_l[mi], c));
+                if (MV > 0) {
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) f.b[ni] = __builtin_bit_cast(bf16x8, rd(Bs, brow_l[ni], c));
+                }
             }
         };
-        auto mfma_step = [&](const StepFrags& f) {
+        auto mfma_step = [&](const StepFrags<FP8>& f, int kt) {
+            if constexpr (FP8) {
+                // the stage's 128-wide K block is kt (< 64)
+                const int sc_lo = __builtin_amdgcn_readlane(s_lo, kt);
+                const int sc_hi = __builtin_amdgcn_readlane(s_hi, kt);
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                if (mi < MV) {
+                for (int mi = 0; mi < MI; ++mi)
+                    if (mi < MV) {
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
-                }
+                        for (int ni = 0; ni < NI; ++ni) {
+                            const int sb = (MODE == kGateUp && ni >= 2) ? sc_hi : sc_lo;
+                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0, kUnitScale, 0, sb);
+                        }
+                    }
+            } else {
+                (void)kt;
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    if (mi < MV) {
+#pragma unroll
+                        for (int ni = 0; ni < NI; ++ni)
+                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+                    }
+            }
         };
 
-        StepFrags f0, f1;
+        StepFrags<FP8> f0, f1;
         // prologue: A0 B0 A1 B1 B2 in this order; wait for stage 0 (A0, B0)
         dma_a(0, 0);
         dma_b(0, 0);
@@ -218,10 +282,10 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             // K steps 0 .. KS-2 (KS is even, so the buffers alternate statically)
 #pragma unroll
             for (int s = 0; s + 1 < KS; ++s) {
-                StepFrags& cur = (s & 1) ? f1 : f0;
-                StepFrags& nxt = (s & 1) ? f0 : f1;
+                StepFrags<FP8>& cur = (s & 1) ? f1 : f0;
+                StepFrags<FP8>& nxt = (s & 1) ? f0 : f1;
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_step(cur);
+                mfma_step(cur, kt);
                 load_frags(nxt, aslot, bslot, s + 1);
                 sched_interleave<NM, NR, 0>();
                 __builtin_amdgcn_sched_barrier(0);
@@ -234,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             if (kt + 2 < nk) dma_a(aslot, kt + 2);        // into the slots stage kt drained
             if (kt + 3 < nk) dma_b(bslot, kt + 3);
-            mfma_step(f1);
+            mfma_step(f1, kt);
             if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
             // the loads first (two after each of the first MFMAs; PER is even), then the
             // fragment reads of stage kt + 1
@@ -257,7 +321,11 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         for (int i = 0; i < 16; ++i) {
             const int m = (wm + 2 * mi) * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
             if (m >= rows) continue;
-            constexpr float sa = 1.0f;
+            float sa = 1.0f;
+            if constexpr (FP8) {
+                const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
+                sa = g.a_scale[ar];
+            }
             uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
             if constexpr (SPLIT) {
                 // FP32 partial sums of the slice: gate then up sums for gate/up (the SwiGLU
@@ -290,11 +358,11 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     }
 }
 
-template <int MODE, bool GATHER, bool SPLIT>
+template <int MODE, bool GATHER, bool FP8, bool SPLIT>
 static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
     static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, SPLIT>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, SPLIT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kWideLds));
         attr_set = true;
     }
@@ -302,37 +370,39 @@ static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int block
     if (SPLIT) {
         GroupedGemmArgs gs = g;
         gs.k_slices = ks;
-        gemm_wide<MODE, GATHER, SPLIT><<<blocks, 256, lds, st>>>(gs);
+        gemm_wide<MODE, GATHER, FP8, SPLIT><<<blocks, 256, lds, st>>>(gs);
     } else {
-        gemm_wide<MODE, GATHER, SPLIT><<<blocks, 256, lds, st>>>(g);
+        gemm_wide<MODE, GATHER, FP8, SPLIT><<<blocks, 256, lds, st>>>(g);
     }
 }
 
+template <bool FP8>
 static void launch_wide_modes(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks, int ks) {
     // split K only for a single weight set (rows in token order, no gather); the grid
     // enumerates every (row tile bound, column tile, slice)
     if (ks > 1) {
         const int ncol = (mode == kGateUp) ? 128 : 256;
         const int nb = g.max_tiles * (g.n_out / ncol) * ks;
-        if (mode == kGateUp) launch_wide_inst<kGateUp, false, true>(st, g, nb, ks);
-        else launch_wide_inst<kDown, false, true>(st, g, nb, ks);
+        if (mode == kGateUp) launch_wide_inst<kGateUp, false, FP8, true>(st, g, nb, ks);
+        else launch_wide_inst<kDown, false, FP8, true>(st, g, nb, ks);
     } else if (mode == kGateUp) {
-        if (g.gather) launch_wide_inst<kGateUp, true, false>(st, g, blocks, 1);
-        else launch_wide_inst<kGateUp, false, false>(st, g, blocks, 1);
+        if (g.gather) launch_wide_inst<kGateUp, true, FP8, false>(st, g, blocks, 1);
+        else launch_wide_inst<kGateUp, false, FP8, false>(st, g, blocks, 1);
     } else {
-        if (g.gather) launch_wide_inst<kDown, true, false>(st, g, blocks, 1);
-        else launch_wide_inst<kDown, false, false>(st, g, blocks, 1);
+        if (g.gather) launch_wide_inst<kDown, true, FP8, false>(st, g, blocks, 1);
+        else launch_wide_inst<kDown, false, FP8, false>(st, g, blocks, 1);
     }
 }
 
-int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g) {
+int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8) {
     if (g.max_tiles == 0) return 1;
     const int ncol = (mode == kGateUp) ? 128 : 256;
     // every (row tile, column tile) of whole groups of group_m row tiles, in whole XCD chunks
     const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
     const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
-    const int ks = prefill_k_split(mode, g, PrefillWeights::kBf16);
-    launch_wide_modes(st, mode, g, blocks, ks);
+    const int ks = prefill_k_split(mode, g, fp8 ? PrefillWeights::kFp8 : PrefillWeights::kBf16);
+    if (fp8) launch_wide_modes<true>(st, mode, g, blocks, ks);
+    else launch_wide_modes<false>(st, mode, g, blocks, ks);
     return ks;
 }
 

@@ -124,8 +124,9 @@ constexpr int kFp8PrefillMaxKd = 32768;     // LDS holds the K-block scale codes
 // prefill_k_split gives beforehand.  MXFP4 slices hold at most kMxfp4PrefillMaxKd of K.
 int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
 int prefill_k_split(GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt);
-// gemm_wide.hip: the same GEMMs for BF16 weights with 128-byte K stages
-int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g);
+// gemm_wide.hip: the same GEMMs for BF16 or FP8 weights (FP8: K <= 8192) with 128-byte
+// K stages
+int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bool fp8);
 // gemm_wide_mx.hip: the same for MXFP4 weights with 128-value K stages, for K slices of at
 // most 6144 (wide_mx_supported); ks = prefill_k_split(mode, g, kMxfp4)
 bool wide_mx_supported(const GroupedGemmArgs& g, int ks);
