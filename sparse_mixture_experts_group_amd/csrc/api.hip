@@ -282,7 +282,7 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
     // tokens spread over the experts, or at most 16 rows of the dense MLP's single weight
     // set (the streaming kernels read the weights once per 32 rows)
     const bool decode = dense ? T <= kDenseStreamMaxT
-                              : T <= (c.weight_dtype == BEAM_DTYPE_BF16 ? kBf16StreamMaxT : kDecodeMaxT);
+                              : T <= (c.weight_dtype == BEAM_DTYPE_MXFP4 ? kDecodeMaxT : kWideStreamMaxT);
     if (dense && c.weight_dtype != BEAM_DTYPE_F32) {
         g1.part = g2.part = at<float>(ws, L.part);
         g1.part_cap = g2.part_cap = dense_part_floats(c, T);

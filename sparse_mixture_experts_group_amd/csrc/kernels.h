@@ -25,7 +25,7 @@ __host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
     return static_cast<int>((j * m / nt) * 32);
 }
 constexpr int kDecodeMaxT = 256;    // token counts up to this use the streaming GEMMs
-constexpr int kBf16StreamMaxT = 127;   // the same with BF16 weights (the 128-byte-stage tiled GEMM wins above)
+constexpr int kWideStreamMaxT = 127;   // the same with BF16 or FP8 weights (the 128-byte-stage tiled GEMM wins above)
 constexpr int kDenseStreamMaxT = 16;   // the same for the dense MLP (all rows on one weight set)
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of

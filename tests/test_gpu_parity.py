@@ -271,10 +271,10 @@ def test_fp8_sublayer():
     assert e_h <= TOL[DT_FP8]
 
 
-@pytest.mark.parametrize("T", [16, 200, 700])
+@pytest.mark.parametrize("T", [16, 100, 200, 700])
 def test_fp8_forward(T):
-    """FP8 experts through beam_moe_forward: the streaming kernels (T <= 256; 16 or 32
-    rows per pass) and the LDS-tiled kernels with mostly partial tiles (T = 700)."""
+    """FP8 experts through beam_moe_forward: the streaming kernels (T <= 127; 16 or 32
+    rows per pass) and the LDS-tiled kernels with mostly partial tiles (T = 200, 700)."""
     w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192")
     from dataclasses import replace
     from beam_inputs import token_inputs, to_bf16_bits
