@@ -94,7 +94,7 @@ int64_t dense_part_floats(const beam_moe_config& c, int64_t T) {
 }
 
 // Workspace regions.  dense: the dense MLP (c has n_experts = topk = 1): no router
-// regions, and FP32 split-K partial sums for its streaming down GEMM.
+// regions, and FP32 split-K partial sums for its GEMMs.
 Layout make_layout(const beam_moe_config& c, int64_t T, bool dense = false) {
     Layout L;
     const int64_t E = c.n_experts, K = c.topk, H = c.hidden, I = c.inter;
