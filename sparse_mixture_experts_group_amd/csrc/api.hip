@@ -238,21 +238,16 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     return g;
 }
 
-// LDS-tiled GEMMs.  The 128-byte-stage kernel (gemm_wide.hip) for BF16 weights streamed
-// with few rows per expert (tile pairs, the weight-bound regime) and for FP8 weights with
-// fewer than 192 rows per expert on average (wave tiles about half full), the
-// 128-value-stage kernel (gemm_wide_mx.hip) for MXFP4 weights while a K slice fits its
-// LDS scale budget, the 64-byte-stage kernel (gemm_prefill.hip) otherwise: where all
-// four row tiles of a wave are live it is the faster one (measured).  The wide kernels
-// address their operands with 32-bit offsets.  a_rows: rows of the activation matrix;
-// avg_rows: routed rows per expert on average.
-int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt, int64_t a_rows,
-                 int64_t avg_rows) {
+// LDS-tiled GEMMs: the 128-byte-stage kernel (gemm_wide.hip) for BF16 and FP8 weights,
+// the 128-value-stage kernel (gemm_wide_mx.hip) for MXFP4 weights while a K slice fits
+// its LDS scale budget; both address their operands with 32-bit offsets and take FP8
+// reductions of at most 64 scale blocks.  The 64-byte-stage kernel (gemm_prefill.hip)
+// serves the rest.  a_rows: rows of the activation matrix.
+int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt, int64_t a_rows) {
     const int64_t nw = (mode == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const bool fits = a_rows * g.lda * 2 < (int64_t{1} << 32) && nw * g.kd * 2 < (int64_t{1} << 32);
-    if (wt == PrefillWeights::kBf16 && g.group_m == 2 && fits) return launch_gemm_wide(st, mode, g, false);
-    if (wt == PrefillWeights::kFp8 && avg_rows < 192 && g.kd <= 64 * 128 && fits)
-        return launch_gemm_wide(st, mode, g, true);
+    if (wt == PrefillWeights::kBf16 && fits) return launch_gemm_wide(st, mode, g, false);
+    if (wt == PrefillWeights::kFp8 && g.kd <= 64 * 128 && fits) return launch_gemm_wide(st, mode, g, true);
     if (wt == PrefillWeights::kMxfp4 && fits) {
         const int ks = prefill_k_split(mode, g, wt);
         if (wide_mx_supported(g, ks)) return launch_gemm_wide_mx(st, mode, g, ks);
@@ -303,20 +298,20 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) slices1 = launch_gemm_bf16_decode(st, kGateUp, g1);
-            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kBf16, T, P / c.n_experts);
+            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kBf16, T);
         }
         swiglu();
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) slices = launch_gemm_bf16_decode(st, kDown, g2);
-            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kBf16, P, P / c.n_experts);
+            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kBf16, P);
         }
     } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) slices1 = launch_gemm_fp8_decode(st, kGateUp, g1);
-            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kFp8, T, P / c.n_experts);
+            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kFp8, T);
         }
         swiglu();
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
@@ -324,13 +319,13 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) slices = launch_gemm_fp8_decode(st, kDown, g2);
-            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kFp8, P, P / c.n_experts);
+            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kFp8, P);
         }
     } else {            // MXFP4 weights
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
             if (decode) slices1 = launch_gemm_mxfp4_decode(st, kGateUp, g1);
-            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kMxfp4, T, P / c.n_experts);
+            else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kMxfp4, T);
         }
         swiglu();
         launch_quant_rows_fp8(st, P, I, true, at<void>(ws, L.hbuf), at<uint8_t>(ws, L.h8), at<float>(ws, L.h8s));
@@ -338,7 +333,7 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
             if (decode) slices = launch_gemm_mxfp4_decode(st, kDown, g2);
-            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kMxfp4, P, P / c.n_experts);
+            else slices = launch_tiled(st, kDown, g2, PrefillWeights::kMxfp4, P);
         }
     }
     if (slices > 1) launch_splitk_reduce(st, slices, P * H, g2.part_slice, g2.part, static_cast<uint16_t*>(down_out));

@@ -18,11 +18,10 @@
 // and shared weight panels come from L2.  A stage is 32 KB of activations (256 rows x
 // 128 bytes) and 32 KB of weights; the 160 KB of LDS hold two activation slots and three
 // weight slots, so while stage j is computed the activations of stage j + 1 and the
-// weights of stages j + 1 and j + 2 (the HBM stream) are in flight.  (Measured on the
-// Beam layer it beats the 64-byte-stage kernel where BF16 weights stream from HBM with
-// few rows per expert -- 4096 tokens: gate/up 2.65 against 2.83 ms, down 1.49 against
-// 1.60 -- and loses where all four row tiles of a wave are live, e.g. FP8 weights at
-// 8192 tokens, 3.01 against 2.73 ms.)
+// weights of stages j + 1 and j + 2 (the HBM stream) are in flight.  Measured on the
+// Beam layer against the 64-byte-stage kernel: 4096 tokens (BF16) gate/up 2.53 against
+// 2.83 ms, 32768 skewed tokens 13.67 against 13.71, 8192 tokens with FP8 weights 2.55
+// against 2.72.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -262,17 +261,17 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         };
 
         StepFrags<FP8> f0, f1;
-        // prologue: A0 B0 A1 B1 B2 in this order; wait for stage 0 (A0, B0)
+        // The loop body is branch-free (a branch would split the fragment registers into
+        // copies at its join): stage indices past the end are clamped, and the last
+        // iterations re-load the last stage into slots nothing reads any more, so every
+        // stage issues the same loads and every wait count is fixed.
+        // Prologue order: A0 B0 A1 B1 B2; wait for stage 0 (A0, B0).
         dma_a(0, 0);
         dma_b(0, 0);
-        if (nk > 1) {
-            dma_a(1, 1);
-            dma_b(1, 1);
-        }
-        if (nk > 2) dma_b(2, 2);
-        if (nk > 2) wait_lds_dma<2 * MV + 16>();
-        else if (nk > 1) wait_lds_dma<2 * MV + 8>();
-        else wait_lds_dma<0>();
+        dma_a(1, min(1, nk - 1));
+        dma_b(1, min(1, nk - 1));
+        dma_b(2, min(2, nk - 1));
+        wait_lds_dma<2 * MV + 16>();
         lds_pipeline_barrier();
         load_frags(f0, 0, 0, 0);
         int bslot = 0;                                   // weight slot of stage kt (kt % 3)
@@ -292,14 +291,13 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             }
             // last K step.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has
             // landed once at most the 8 weight loads of stage kt + 2 are in flight.
-            if (kt + 2 < nk) wait_lds_dma<8>();
-            else wait_lds_dma<0>();
+            wait_lds_dma<8>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (kt + 2 < nk) dma_a(aslot, kt + 2);        // into the slots stage kt drained
-            if (kt + 3 < nk) dma_b(bslot, kt + 3);
+            dma_a(aslot, min(kt + 2, nk - 1));           // into the slots stage kt drained
+            dma_b(bslot, min(kt + 3, nk - 1));
             mfma_step(f1, kt);
-            if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
+            load_frags(f0, aslot ^ 1, bnext, 0);
             // the loads first (two after each of the first MFMAs; PER is even), then the
             // fragment reads of stage kt + 1
 #pragma unroll
@@ -311,6 +309,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             bslot = bnext;
         }
+        wait_lds_dma<0>();      // the tail's re-loads land before the block's LDS is released
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
 

@@ -217,17 +217,17 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
         };
 
         MxFrags f0, f1;
-        // prologue: A0 B0 A1 B1 B2 in this order; wait for stage 0 (A0, B0)
+        // The loop body is branch-free (a branch would split the fragment registers into
+        // copies at its join): stage indices past the end are clamped, and the last
+        // iterations re-load the last stage into slots nothing reads any more, so every
+        // stage issues the same loads and every wait count is fixed.
+        // Prologue order: A0 B0 A1 B1 B2; wait for stage 0 (A0, B0).
         dma_a(0, 0);
         dma_b(0, 0);
-        if (nk > 1) {
-            dma_a(1, 1);
-            dma_b(1, 1);
-        }
-        if (nk > 2) dma_b(2, 2);
-        if (nk > 2) wait_lds_dma<2 * MV + 8>();
-        else if (nk > 1) wait_lds_dma<2 * MV + 4>();
-        else wait_lds_dma<0>();
+        dma_a(1, min(1, nk - 1));
+        dma_b(1, min(1, nk - 1));
+        dma_b(2, min(2, nk - 1));
+        wait_lds_dma<2 * MV + 8>();
         lds_pipeline_barrier();
         load_frags(f0, 0, 0, 0);
         int bslot = 0;                                   // weight slot of stage kt (kt % 3)
@@ -241,14 +241,13 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             // step 1.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has landed
             // once at most the 4 weight loads of stage kt + 2 are in flight.
-            if (kt + 2 < nk) wait_lds_dma<4>();
-            else wait_lds_dma<0>();
+            wait_lds_dma<4>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (kt + 2 < nk) dma_a(aslot, kt + 2);        // into the slots stage kt drained
-            if (kt + 3 < nk) dma_b(bslot, kt + 3);
+            dma_a(aslot, min(kt + 2, nk - 1));           // into the slots stage kt drained
+            dma_b(bslot, min(kt + 3, nk - 1));
             mfma_step(f1, kt, 1);
-            if (kt + 1 < nk) load_frags(f0, aslot ^ 1, bnext, 0);
+            load_frags(f0, aslot ^ 1, bnext, 0);
             // the loads first (two after each of the first MFMAs; PER is even), then the
             // fragment reads of stage kt + 1
 #pragma unroll
@@ -260,6 +259,7 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             bslot = bnext;
         }
+        wait_lds_dma<0>();      // the tail's re-loads land before the block's LDS is released
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
 
