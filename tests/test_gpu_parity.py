@@ -401,12 +401,24 @@ _EDGE = {
     "two_experts": dict(H=128, I=64, E=2, G=1, Kg=1, K=2, act_dtype=DT_F32, weight_dtype=DT_F32),
     # register-tiled router logits with 16-deep tiles (chunks of 16 hidden entries)
     "short_chunks": dict(H=1024, I=256, E=128, G=8, Kg=4, K=8),
+    # FP8 reductions over more than 64 scale blocks (the 64-byte-stage GEMM with its
+    # block scales in LDS): gate/up over H = 8448, down over I = 8448
+    "fp8_long_hidden": dict(H=8448, I=256, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8),
+    "fp8_long_inter": dict(H=256, I=8448, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8),
+    # MXFP4 K slices longer than 6144 (the 64-byte-stage GEMM)
+    "mxfp4_long_hidden": dict(H=6656, I=512, E=16, G=4, Kg=2, K=4, weight_dtype=DT_MXFP4),
+    "mxfp4_long_inter": dict(H=512, I=6656, E=16, G=4, Kg=2, K=4, weight_dtype=DT_MXFP4),
+    # 2^20 routed rows x I = 2560: the down GEMM's activations span 5.4 GB, past the
+    # 32-bit offsets of the 128-byte-stage GEMM (the 64-byte-stage one, 64-bit addresses)
+    "rows_past_4gb": dict(H=256, I=2560, E=64, G=8, Kg=4, K=32),
 }
 
 
 @pytest.mark.parametrize("case,T", [("max_hidden_topk", 16), ("max_hidden_topk", 300), ("single_group", 100),
                                     ("single_group", 700), ("all_groups_kept", 64), ("k1", 50),
-                                    ("two_experts", 40), ("short_chunks", 4096), ("short_chunks", 16384)])
+                                    ("two_experts", 40), ("short_chunks", 4096), ("short_chunks", 16384),
+                                    ("fp8_long_hidden", 300), ("fp8_long_inter", 300), ("mxfp4_long_hidden", 300),
+                                    ("mxfp4_long_inter", 300), ("rows_past_4gb", 32768)])
 def test_config_limits_and_degenerate_routing(case, T):
     from beam_inputs import Workload, make_inputs
     w = Workload(f"edge_{case}", T=T, seed=3, x_recipe="rms_normal", **_EDGE[case])
@@ -419,6 +431,9 @@ def test_config_limits_and_degenerate_routing(case, T):
     else:
         dev["w13"] = torch.from_numpy(full.w13).cuda()
         dev["w2"] = torch.from_numpy(full.w2).cuda()
+    if full.w13_scale is not None:
+        dev["w13_scale"] = torch.from_numpy(full.w13_scale).cuda()
+        dev["w2_scale"] = torch.from_numpy(full.w2_scale).cuda()
     cfg, y, ids, wts, ws = run_forward(w, dev, full.x, None)
     tok = np.arange(T) if T <= 1000 else sample_tokens(T)
     ref = oracle.moe_forward(x_f32(w, full.x), full.w_router, None, bank_of(w, full), w.G, w.Kg, w.K, w.alpha,
