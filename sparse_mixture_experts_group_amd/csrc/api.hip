@@ -243,7 +243,9 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
 // its LDS scale budget; both address their operands with 32-bit offsets and take FP8
 // reductions of at most 64 scale blocks.  The 64-byte-stage kernel (gemm_prefill.hip)
 // serves the rest.  a_rows: rows of the activation matrix.
-int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, PrefillWeights wt, int64_t a_rows) {
+int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& ga, PrefillWeights wt, int64_t a_rows) {
+    GroupedGemmArgs g = ga;
+    g.a_rows = a_rows;
     const int64_t nw = (mode == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const bool fits = a_rows * g.lda * 2 < (int64_t{1} << 32) && nw * g.kd * 2 < (int64_t{1} << 32);
     if (wt == PrefillWeights::kBf16 && fits) return launch_gemm_wide(st, mode, g, false);

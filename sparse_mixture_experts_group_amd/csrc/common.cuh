@@ -132,6 +132,53 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
 }
 
+// A buffer resource over `bytes` bytes from `base` (raw addressing: loads whose offset
+// reaches `bytes` return zeros instead of touching memory).  bytes < 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    // dword 3: a 32-bit data format, as raw dword loads require on gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(static_cast<uint32_t>(bytes)),
+                                             0x00020000);
+}
+
+// The buffer form of lds_dma16: lane i's 16 bytes from rsrc base + soff + voff (voff per
+// lane, soff wave-uniform) land at lds_dst + 16 i.  32-bit offsets, no per-lane 64-bit
+// address arithmetic.
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds_dst), 16,
+                                             static_cast<int>(voff), soff, 0, 0);
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>{}) for i = I .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Scheduling pattern for one K step of NM MFMAs whose next fragments are read before
+// its global loads are issued (program order; the compiler keeps LDS reads ahead of
+// direct-to-LDS loads it cannot tell apart from them): NR LDS reads spread over the
+// first half of the MFMAs, NV loads over the second half, so no MFMA waits behind a
+// burst of load issues.
+template <int NM, int NR, int NV>
+__device__ __forceinline__ void sched_reads_then_loads() {
+    constexpr int H1 = NM / 2 > 0 ? NM / 2 : 1, H2 = NM - H1 > 0 ? NM - H1 : 1;
+    static_for<0, NM>([](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              // MFMA
+        if constexpr (i < H1) {
+            constexpr int nr = ((i + 1) * NR) / H1 - (i * NR) / H1;
+            if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // DS read
+        } else {
+            constexpr int j = i - H1;
+            constexpr int nv = ((j + 1) * NV) / H2 - (j * NV) / H2;
+            if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // VMEM
+        }
+    });
+}
+
 // s_waitcnt vmcnt(N) (expcnt / lgkmcnt left alone): all but the N most recent
 // direct-to-LDS loads this wave issued have landed in LDS.  gfx9 encoding: vmcnt bits
 // [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15 (no wait).

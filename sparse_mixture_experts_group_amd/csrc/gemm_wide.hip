@@ -22,6 +22,13 @@
 // Beam layer against the 64-byte-stage kernel: 4096 tokens (BF16) gate/up 2.53 against
 // 2.83 ms, 32768 skewed tokens 13.67 against 13.71, 8192 tokens with FP8 weights 2.55
 // against 2.72.
+//
+// Load issue: a 16-byte-per-lane load holds the wave's issue for many cycles, so a burst
+// of them leaves the matrix pipe idle (counters: MFMA busy 55% of the time with the 16
+// loads of a stage issued two per MFMA, 77% with none).  The loads are buffer loads
+// (32-bit lane offsets fixed per block, the stage advance in a scalar offset) spread
+// over the MFMAs of the whole stage: skewed 32768 tokens gate/up 13.46 -> 12.11 ms,
+// dense MLP at 4096 tokens 2.41 -> 2.19 ms per step.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -66,12 +73,13 @@ template <> struct StepFrags<true> { i32x8 a[4]; i32x8 b[4]; };
 
 // Pipeline per stage kt (KS MFMA K steps: 4 of 16 for BF16, 2 of 64 for FP8), fragments double
 // buffered in registers: K steps 0 .. KS-2 run their MFMAs while reading the next step's
-// fragments from the stage's slots; before the last step every wave waits until stage
+// fragments from the stage's slots and loading a share of the weights of stage kt + 2
+// into the slot stage kt - 1 drained; before the last step every wave waits until stage
 // kt + 1 has landed (only the weight loads of stage kt + 2 may still be in flight) and
-// meets the others, then loads the activations of stage kt + 2 and the weights of stage
-// kt + 3 into the slots stage kt drained, runs the last step's MFMAs and reads stage
-// kt + 1's first fragments.  FP8: one 128 x 128 scale block per stage, at most 64 per
-// reduction (a lane of a register each).
+// meets the others, then runs the last step's MFMAs while reading stage kt + 1's first
+// fragments and loading the activations of stage kt + 2 into the slot stage kt drained.
+// FP8: one 128 x 128 scale block per stage, at most 64 per reduction (a lane of a
+// register each).
 //
 // SPLIT: as in gemm_prefill.hip, the GEMMs of a single weight set split K into
 // g.k_slices slices (FP32 partial sums) over a flat block order.
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     const int rows = expert_tile_first(n_e, ti.y + 1, BM) - first;
     const int row0 = g.exp_off[e] + first;
     const int c0 = nt * NCOL;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const int64_t krow = static_cast<int64_t>(g.kd) * EB;        // bytes per weight row
@@ -140,6 +148,8 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     const uint32_t boff = static_cast<uint32_t>(weight_row(wave * 64 + dr) * krow);
     const uint32_t bch0 = wide_dma_chunk(lane, 0), bch1 = wide_dma_chunk(lane, 1);
     const uint32_t bstep = static_cast<uint32_t>(8 * krow);   // bytes between B rows j and j + 1
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(abase, (g.a_rows * g.lda - kbeg) * EB);
+    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(bbase, nw * krow - static_cast<int64_t>(kbeg) * EB);
 
     // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l of the slice
     // (gate-column block in s_lo, up-column block in s_hi for gate/up; this wave's column
@@ -183,26 +193,28 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
 
     auto k_loop = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
-        constexpr int PER = 2 * MV + 8;                 // direct-to-LDS loads per stage and wave
         constexpr int NM = MV * NI;                      // MFMAs per K step
         constexpr int NR = MV == 0 ? 0 : (FP8 ? 2 : 1) * (MV + NI);   // LDS reads per K step
         auto dma_a = [&](int slot, int kt) {            // activations of stage kt
             uint8_t* As = smem + slot * kWideOpBytes;
-            const uint8_t* ak = abase + static_cast<int64_t>(kt) * kWideRowBytes;
+            const int ks = kt * kWideRowBytes;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
                 if (i < MV) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        lds_dma16(ak + aoff[i][h], As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kWideRowBytes);
+                        lds_dma16_buf(rsrc_a, As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kWideRowBytes, aoff[i][h], ks);
                 }
         };
-        auto dma_b = [&](int slot, int kt) {            // weights of stage kt (8 loads)
+        // weights of stage kt: loads J0 .. J1 - 1 of the wave's 8
+        auto dma_b = [&](int slot, int kt, auto j0_tag, auto j1_tag) {
+            constexpr int J0 = decltype(j0_tag)::value, J1 = decltype(j1_tag)::value;
             uint8_t* Bs = smem + (kWideASlots + slot) * kWideOpBytes;
-            const uint8_t* bk = bbase + static_cast<int64_t>(kt) * kWideRowBytes;
+            const int ks = kt * kWideRowBytes;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                lds_dma16(bk + (boff + j * bstep + ((j & 1) ? bch1 : bch0)), Bs + (wave * 64 + 8 * j) * kWideRowBytes);
+            for (int j = J0; j < J1; ++j)
+                lds_dma16_buf(rsrc_b, Bs + (wave * 64 + 8 * j) * kWideRowBytes, boff + j * bstep + ((j & 1) ? bch1 : bch0),
+                              ks);
         };
         auto rd = [&](const uint8_t* T, int row, int c) {
             return *reinterpret_cast<const u32x4*>(T + wide_offset(row, c));
@@ -265,47 +277,45 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         // copies at its join): stage indices past the end are clamped, and the last
         // iterations re-load the last stage into slots nothing reads any more, so every
         // stage issues the same loads and every wait count is fixed.
-        // Prologue order: A0 B0 A1 B1 B2; wait for stage 0 (A0, B0).
+        // Prologue order: A0 B0 A1 B1; wait for stage 0 (A0, B0).  Issue order in the
+        // loop: B(kt + 2) during the first K steps of stage kt, A(kt + 2) in its last.
+        using I0 = std::integral_constant<int, 0>;
+        using I8 = std::integral_constant<int, 8>;
         dma_a(0, 0);
-        dma_b(0, 0);
+        dma_b(0, 0, I0{}, I8{});
         dma_a(1, min(1, nk - 1));
-        dma_b(1, min(1, nk - 1));
-        dma_b(2, min(2, nk - 1));
-        wait_lds_dma<2 * MV + 16>();
+        dma_b(1, min(1, nk - 1), I0{}, I8{});
+        wait_lds_dma<2 * MV + 8>();
         lds_pipeline_barrier();
         load_frags(f0, 0, 0, 0);
         int bslot = 0;                                   // weight slot of stage kt (kt % 3)
         for (int kt = 0; kt < nk; ++kt) {
             const int aslot = kt & 1;
             const int bnext = (bslot == kWideBSlots - 1) ? 0 : bslot + 1;
-            // K steps 0 .. KS-2 (KS is even, so the buffers alternate statically)
-#pragma unroll
-            for (int s = 0; s + 1 < KS; ++s) {
+            const int bfree = (bslot == 0) ? kWideBSlots - 1 : bslot - 1;   // stage kt - 1's slot
+            // K steps 0 .. KS-2 (KS is even, so the buffers alternate statically): the next
+            // step's fragments, then a share of the weights of stage kt + 2
+            static_for<0, KS - 1>([&](auto s_tag) {
+                constexpr int s = decltype(s_tag)::value;
+                constexpr int j0 = (8 * s) / (KS - 1), j1 = (8 * (s + 1)) / (KS - 1);
                 StepFrags<FP8>& cur = (s & 1) ? f1 : f0;
                 StepFrags<FP8>& nxt = (s & 1) ? f0 : f1;
                 __builtin_amdgcn_sched_barrier(0);
                 mfma_step(cur, kt);
                 load_frags(nxt, aslot, bslot, s + 1);
-                sched_interleave<NM, NR, 0>();
+                dma_b(bfree, min(kt + 2, nk - 1), std::integral_constant<int, j0>{}, std::integral_constant<int, j1>{});
+                sched_reads_then_loads<NM, NR, j1 - j0>();
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
             // last K step.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has
             // landed once at most the 8 weight loads of stage kt + 2 are in flight.
             wait_lds_dma<8>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            dma_a(aslot, min(kt + 2, nk - 1));           // into the slots stage kt drained
-            dma_b(bslot, min(kt + 3, nk - 1));
             mfma_step(f1, kt);
             load_frags(f0, aslot ^ 1, bnext, 0);
-            // the loads first (two after each of the first MFMAs; PER is even), then the
-            // fragment reads of stage kt + 1
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                if (2 * i < PER) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // VMEM
-                else if (i - PER / 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
+            dma_a(aslot, min(kt + 2, nk - 1));           // into the slot stage kt drained
+            sched_reads_then_loads<NM, NR, 2 * MV>();
             __builtin_amdgcn_sched_barrier(0);
             bslot = bnext;
         }

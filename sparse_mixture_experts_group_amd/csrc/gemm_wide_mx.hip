@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
     const int rows = expert_tile_first(n_e, ti.y + 1, BM) - first;
     const int row0 = g.exp_off[e] + first;
     const int c0 = nt * NCOL;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t nw = (MODE == kGateUp) ? 2 * static_cast<int64_t>(g.n_out) : g.n_out;
     const int64_t krow = g.kd / 2;                               // weight bytes per row
@@ -130,6 +130,8 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
     const uint8_t* bbase = static_cast<const uint8_t*>(g.w) + static_cast<int64_t>(e) * nw * krow + kbeg / 2;
     const uint32_t boff = static_cast<uint32_t>(weight_row(wave * 64 + (lane >> 2)) * krow) + dma_chunk_offset(lane);
     const uint32_t bstep = static_cast<uint32_t>(16 * krow);   // bytes between B rows j and j + 1
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(abase, g.a_rows * g.lda - kbeg);
+    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(bbase, nw * krow - kbeg / 2);
 
     // The tile's E8M0 block scales of its K slice: 256 weight rows x klen / 32 codes after
     // the operand slots (thread t copies row t).
@@ -165,25 +167,24 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
 
     auto k_loop = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
-        constexpr int PER = 2 * MV + 4;                 // direct-to-LDS loads per stage and wave
         constexpr int NM = MV * NI;                      // MFMAs per K step
         constexpr int NR = MV == 0 ? 0 : 2 * MV + NI;    // LDS reads per K step
         auto dma_a = [&](int slot, int kt) {            // activations of stage kt
             uint8_t* As = smem + slot * kMxASlotBytes;
-            const uint8_t* ak = abase + static_cast<int64_t>(kt) * kMxARowBytes;
+            const int ks = kt * kMxARowBytes;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
                 if (i < MV) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        lds_dma16(ak + aoff[i][h], As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kMxARowBytes);
+                        lds_dma16_buf(rsrc_a, As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kMxARowBytes, aoff[i][h], ks);
                 }
         };
         auto dma_b = [&](int slot, int kt) {            // weights of stage kt (4 loads)
             uint8_t* Bs = smem + kMxASlots * kMxASlotBytes + slot * kMxBSlotBytes;
-            const uint8_t* bk = bbase + static_cast<int64_t>(kt) * kMxBRowBytes;
+            const int ks = kt * kMxBRowBytes;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lds_dma16(bk + (boff + j * bstep), Bs + (wave * 64 + 16 * j) * kMxBRowBytes);
+            for (int j = 0; j < 4; ++j) lds_dma16_buf(rsrc_b, Bs + (wave * 64 + 16 * j) * kMxBRowBytes, boff + j * bstep, ks);
         };
         // fragments of K step s (64 values) of a stage whose operands sit in aslot, bslot
         auto load_frags = [&](MxFrags& f, int aslot, int bslot, int s) {
@@ -221,41 +222,38 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
         // copies at its join): stage indices past the end are clamped, and the last
         // iterations re-load the last stage into slots nothing reads any more, so every
         // stage issues the same loads and every wait count is fixed.
-        // Prologue order: A0 B0 A1 B1 B2; wait for stage 0 (A0, B0).
+        // Prologue order: A0 B0 A1 B1; wait for stage 0 (A0, B0).  Issue order in the
+        // loop: B(kt + 2) during K step 0 of stage kt, A(kt + 2) during step 1.
         dma_a(0, 0);
         dma_b(0, 0);
         dma_a(1, min(1, nk - 1));
         dma_b(1, min(1, nk - 1));
-        dma_b(2, min(2, nk - 1));
-        wait_lds_dma<2 * MV + 8>();
+        wait_lds_dma<2 * MV + 4>();
         lds_pipeline_barrier();
         load_frags(f0, 0, 0, 0);
         int bslot = 0;                                   // weight slot of stage kt (kt % 3)
         for (int kt = 0; kt < nk; ++kt) {
             const int aslot = kt & 1;
             const int bnext = (bslot == kMxBSlots - 1) ? 0 : bslot + 1;
+            const int bfree = (bslot == 0) ? kMxBSlots - 1 : bslot - 1;      // stage kt - 1's slot
+            // step 0: the next step's fragments, then the weights of stage kt + 2
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(f0, kt, 0);
             load_frags(f1, aslot, bslot, 1);
-            sched_interleave<NM, NR, 0>();
+            dma_b(bfree, min(kt + 2, nk - 1));
+            if constexpr (MV > 0) __builtin_amdgcn_sched_group_barrier(0x100, NI, 0);   // the step's scale reads
+            sched_reads_then_loads<NM, NR, 4>();
             __builtin_amdgcn_sched_barrier(0);
             // step 1.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has landed
             // once at most the 4 weight loads of stage kt + 2 are in flight.
             wait_lds_dma<4>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            dma_a(aslot, min(kt + 2, nk - 1));           // into the slots stage kt drained
-            dma_b(bslot, min(kt + 3, nk - 1));
             mfma_step(f1, kt, 1);
             load_frags(f0, aslot ^ 1, bnext, 0);
-            // the loads first (two after each of the first MFMAs; PER is even), then the
-            // fragment reads of stage kt + 1
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                if (2 * i < PER) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // VMEM
-                else if (i - PER / 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
+            dma_a(aslot, min(kt + 2, nk - 1));           // into the slot stage kt drained
+            if constexpr (MV > 0) __builtin_amdgcn_sched_group_barrier(0x100, NI, 0);   // the step's scale reads
+            sched_reads_then_loads<NM, NR, 2 * MV>();
             __builtin_amdgcn_sched_barrier(0);
             bslot = bnext;
         }

@@ -93,6 +93,8 @@ struct GroupedGemmArgs {
     int64_t part_slice;
     int64_t part_cap;
     int k_slices;             // LDS-tiled GEMMs: K slices of a split launch (set by the launcher)
+    int64_t a_rows;           // rows of the activation matrix a (bounds the buffer loads of
+                              // the 128-byte-stage kernels; set by the launcher)
 };
 constexpr int kMaxKSplit = 16;
 
