@@ -6,10 +6,12 @@
 // routed per token"; FP32 SwiGLU product per the "Residual stream" section):
 //   gate/up:  h[r, j] = SiLU(a_r . Wg[j]) * (a_r . Wu[j])   (a_r gathered by token)
 //   down:     y[r, n] = h_r . Wd[n]
-// Tiles, wave roles, MFMAs, epilogue and block order are those of the 64-byte-stage
-// kernel in gemm_prefill.hip (which serves the other cases): 256 x 256 output
-// tiles of one expert, 4 waves of 128 x 128 as 4 x 4 MFMA tiles of 32 x 32, gate and up
-// rows of the same columns in one tile so the SwiGLU is applied in registers.
+// Tiles, wave roles and block order are those of the 64-byte-stage kernel in
+// gemm_prefill.hip (which serves the other cases): 256 x 256 output tiles of one expert,
+// 4 waves of 128 x 128 as 4 x 4 MFMA tiles of 32 x 32, gate and up rows of the same
+// columns in one tile so the SwiGLU is applied in registers.  The MFMAs take the weights
+// as their A operand and so compute the transposed tile, whose lane layout lets the
+// epilogue (tile_epilogue.cuh) store 4 columns of a row at a time.
 //
 // Why 128-byte stages: a direct global->LDS load moves 16 bytes per lane; with 64-byte
 // row pieces every request covers half an L2 line, and measured on gfx950 the L2 then
@@ -31,6 +33,7 @@
 // dense MLP at 4096 tokens 2.41 -> 2.19 ms per step.
 #include "common.cuh"
 #include "kernels.h"
+#include "tile_epilogue.cuh"
 
 namespace beam {
 
@@ -40,6 +43,7 @@ constexpr int kWideOpBytes = 256 * kWideRowBytes;     // one operand (256 rows) 
 constexpr int kWideASlots = 2, kWideBSlots = 3;
 constexpr size_t kWideLds = (kWideASlots + kWideBSlots) * static_cast<size_t>(kWideOpBytes);
 static_assert(kWideLds <= 160 * 1024, "LDS budget");
+static_assert(kWideLds >= wide_epilogue_lds(kDown) && kWideLds >= wide_epilogue_lds(kGateUp), "epilogue staging");
 
 // 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7): the 16 consecutive rows one
 // fragment read serves per LDS cycle (same chunk) fill both halves of the 256-byte bank
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                         for (int ni = 0; ni < NI; ++ni) {
                             const int sb = (MODE == kGateUp && ni >= 2) ? sc_hi : sc_lo;
                             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0, kUnitScale, 0, sb);
+                                f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, sb, 0, kUnitScale);
                         }
                     }
             } else {
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                     if (mi < MV) {
 #pragma unroll
                         for (int ni = 0; ni < NI; ++ni)
-                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
                     }
             }
         };
@@ -323,47 +327,13 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
 
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = (wm + 2 * mi) * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
-            if (m >= rows) continue;
-            float sa = 1.0f;
-            if constexpr (FP8) {
-                const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
-                sa = g.a_scale[ar];
-            }
-            uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
-            if constexpr (SPLIT) {
-                // FP32 partial sums of the slice: gate then up sums for gate/up (the SwiGLU
-                // follows the reduction)
-                float* prow = g.part + kz * g.part_slice +
-                              static_cast<int64_t>(row0 + m) * (MODE == kGateUp ? 2 * g.n_out : g.ldo);
-                if (MODE == kGateUp) {
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        prow[c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni][i] * sa;
-                        prow[g.n_out + c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni + 2][i] * sa;
-                    }
-                } else {
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) prow[c0 + wn * 128 + ni * 32 + l32] = acc[mi][ni][i] * sa;
-                }
-                continue;
-            }
-            if (MODE == kGateUp) {
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    orow[c0 + wn * 64 + ni * 32 + l32] =
-                        f32_to_bf16_bits(silu(acc[mi][ni][i] * sa) * (acc[mi][ni + 2][i] * sa));
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
-            }
-        }
+    // down: 256-byte row segments per wave, staged through LDS for whole-row stores;
+    // gate/up (128-byte segments) and FP32 partial sums: stored from the registers
+    if constexpr (SPLIT || MODE == kGateUp) {
+        store_wide_tile<MODE, GATHER, FP8, SPLIT>(g, acc, rows, row0, c0, wm, wn, lane, kz);
+    } else {
+        __syncthreads();                 // every wave is out of its K loop: the LDS is free
+        store_wide_tile_bf16<MODE, GATHER, FP8>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
     }
 }
 

@@ -6,11 +6,13 @@
 // routed per token"; FP32 SwiGLU product per the "Residual stream" section):
 //   gate/up:  h[r, j] = SiLU(a_r . Wg[j]) * (a_r . Wu[j])   (a_r gathered by token)
 //   down:     y[r, n] = h_r . Wd[n]
-// Tiles, wave roles, block order and epilogue are those of gemm_prefill.hip; the MFMA is
-// v_mfma_scale_f32_32x32x64_f8f6f4 with an FP4 B operand whose lane holds one 32-value MX
-// block of its column and takes that block's E8M0 byte as its scale (the operand layout
-// measured on gfx950; the E4M3 A lane that pairs with it holds K 16 h .. 16 h + 15 and
-// 32 + 16 h .. 32 + 16 h + 15 of the 64-wide step, h the lane's half).
+// Tiles, wave roles and block order are those of gemm_prefill.hip; the MFMA is
+// v_mfma_scale_f32_32x32x64_f8f6f4 computing the transposed tile (the epilogue of
+// tile_epilogue.cuh) with the FP4 weights as its A operand: a lane holds one 32-value MX
+// block of its weight row and takes that block's E8M0 byte as its scale (the FP4 lane
+// layout measured on gfx950, the same for either operand; the E4M3 activation lane that
+// pairs with it holds K 16 h .. 16 h + 15 and 32 + 16 h .. 32 + 16 h + 15 of the 64-wide
+// step, h the lane's half).
 //
 // Why 128-value stages: the 64-value stages of gemm_prefill.hip fetch FP4 weight rows in
 // 32-byte pieces, a quarter of an L2 line per request; here a stage holds 128 bytes of
@@ -19,6 +21,7 @@
 // K slice is at most 6144 long (the launcher splits longer reductions or falls back).
 #include "common.cuh"
 #include "kernels.h"
+#include "tile_epilogue.cuh"
 
 namespace beam {
 
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
                     for (int mi = 0; mi < MI; ++mi)
                         if (mi < MV)
                             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                f.a[mi], bb, acc[mi][ni], 0, 4, 0, kUnitScale, 0, sb);
+                                bb, f.a[mi], acc[mi][ni], 4, 0, 0, sb, 0, kUnitScale);
                 }
             }
         };
@@ -261,44 +264,13 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
 
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = (wm + 2 * mi) * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
-            if (m >= rows) continue;
-            const int64_t ar = GATHER ? g.pair_of_row[row0 + m] / g.topk : static_cast<int64_t>(row0 + m);
-            const float sa = g.a_scale[ar];
-            uint16_t* orow = out + static_cast<int64_t>(row0 + m) * g.ldo;
-            if constexpr (SPLIT) {
-                // FP32 partial sums of the slice: gate then up sums for gate/up (the SwiGLU
-                // follows the reduction)
-                float* prow = g.part + kz * g.part_slice +
-                              static_cast<int64_t>(row0 + m) * (MODE == kGateUp ? 2 * g.n_out : g.ldo);
-                if (MODE == kGateUp) {
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        prow[c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni][i] * sa;
-                        prow[g.n_out + c0 + wn * 64 + ni * 32 + l32] = acc[mi][ni + 2][i] * sa;
-                    }
-                } else {
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) prow[c0 + wn * 128 + ni * 32 + l32] = acc[mi][ni][i] * sa;
-                }
-                continue;
-            }
-            if (MODE == kGateUp) {
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    orow[c0 + wn * 64 + ni * 32 + l32] =
-                        f32_to_bf16_bits(silu(acc[mi][ni][i] * sa) * (acc[mi][ni + 2][i] * sa));
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    orow[c0 + wn * 128 + ni * 32 + l32] = f32_to_bf16_bits(acc[mi][ni][i] * sa);
-            }
-        }
+    // down: 256-byte row segments per wave, staged through LDS for whole-row stores;
+    // gate/up (128-byte segments) and FP32 partial sums: stored from the registers
+    if constexpr (SPLIT || MODE == kGateUp) {
+        store_wide_tile<MODE, GATHER, true, SPLIT>(g, acc, rows, row0, c0, wm, wn, lane, kz);
+    } else {
+        __syncthreads();                 // every wave is out of its K loop: the LDS is free
+        store_wide_tile_bf16<MODE, GATHER, true>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
     }
 }
 
@@ -310,7 +282,9 @@ static void launch_wide_mx_inst(hipStream_t st, const GroupedGemmArgs& g, int bl
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    const size_t lds = kMxStageLds + 256 * static_cast<size_t>(g.kd / ks / 32);
+    // the pipeline's slots and scales, or the BF16 epilogue's staging if larger
+    size_t lds = kMxStageLds + 256 * static_cast<size_t>(g.kd / ks / 32);
+    if (!SPLIT && MODE == kDown && lds < wide_epilogue_lds(MODE)) lds = wide_epilogue_lds(MODE);
     if (SPLIT) {
         GroupedGemmArgs gs = g;
         gs.k_slices = ks;
