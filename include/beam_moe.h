@@ -76,8 +76,9 @@ typedef enum {
  *   hidden a multiple of 256 and inter of 128 (fp8_block must be 128);
  *   with V = ceil(n_experts / 64) scores per lane (V in {1, 2, 4}), S % V == 0 and
  *   S / V a power of two.
- *   Above 256 tokens per call: hidden and inter <= 8192 for MXFP4 weights and
- *   <= 32768 for FP8 weights (checked per call).
+ *   Per call, where a GEMM runs LDS-tiled: MXFP4 weights above 256 tokens need
+ *   hidden and inter <= 8192; FP8 weights need hidden <= 32768 above 16 tokens and
+ *   inter <= 32768 above 103 tokens.
  * Beam: {5120, 2560, 256, 8, 4, 8, 2.5f, BF16, BF16 or FP8_E4M3, 128, 1e-6f}.
  */
 typedef struct beam_moe_config {
@@ -138,8 +139,8 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  *              row in the low nibble of byte j, 2j+1 in the high nibble)
  *   w13_scale  FP8: device [E, 2I/128, H/128] FP32 block scales (value = code *
  *              scale of its 128x128 tile).  Each scale must be a normal power of two
- *              (an E8M0 block exponent): above 256 tokens the matrix cores apply only
- *              its exponent field.  MXFP4: device [E, 2I, H/32] uint8 E8M0 codes
+ *              (an E8M0 block exponent): in the LDS-tiled GEMMs (gate/up above 16
+ *              tokens, down above 103) the matrix cores apply only its exponent field.  MXFP4: device [E, 2I, H/32] uint8 E8M0 codes
  *              (value = E2M1 element * 2^(code - 127) of its block of 32 along K).
  *              NULL for F32 and BF16 weights.
  *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous;

@@ -261,6 +261,14 @@ int launch_tiled(hipStream_t st, GemmMode mode, const GroupedGemmArgs& ga, Prefi
 // (yperm for the MoE layer).  dense: the single weight set of the dense MLP (rows are
 // tokens, no gather), whose streaming down GEMM may split K into FP32 partial sums that
 // one more kernel adds up.
+// Largest token count at which GEMM `mode` runs on the streaming kernels.
+int64_t stream_max_t(const beam_moe_config& c, bool dense, GemmMode mode) {
+    if (dense) return kDenseStreamMaxT;
+    if (c.weight_dtype == BEAM_DTYPE_MXFP4) return kDecodeMaxT;
+    if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) return mode == kGateUp ? kFp8GateUpStreamMaxT : kFp8DownStreamMaxT;
+    return mode == kGateUp ? kBf16GateUpStreamMaxT : kBf16DownStreamMaxT;
+}
+
 void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, hipStream_t st,
                  const void* x_exp, const float* x_exp_scale, const void* w13,
                  const void* w13_scale, const void* w2, const void* w2_scale,
@@ -275,11 +283,11 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
     g2.lda = I; g2.gather = false;
     g2.w = w2; g2.w_scale = w2_scale; g2.n_out = H; g2.kd = I;
     g2.out = down_out; g2.ldo = H;
-    // streaming kernels while the rows of an expert are few (measured crossovers): T
-    // tokens spread over the experts, or at most 16 rows of the dense MLP's single weight
-    // set (the streaming kernels read the weights once per 32 rows)
-    const bool decode = dense ? T <= kDenseStreamMaxT
-                              : T <= (c.weight_dtype == BEAM_DTYPE_MXFP4 ? kDecodeMaxT : kWideStreamMaxT);
+    // streaming kernels while the rows of an expert are few (measured crossovers, per
+    // GEMM): T tokens spread over the experts, or at most 16 rows of the dense MLP's
+    // single weight set (the streaming kernels read the weights once per 32 rows)
+    const bool decode1 = T <= stream_max_t(c, dense, kGateUp);
+    const bool decode2 = T <= stream_max_t(c, dense, kDown);
     if (dense && c.weight_dtype != BEAM_DTYPE_F32) {
         g1.part = g2.part = at<float>(ws, L.part);
         g1.part_cap = g2.part_cap = dense_part_floats(c, T);
@@ -299,20 +307,20 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
     } else if (c.weight_dtype == BEAM_DTYPE_BF16) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) slices1 = launch_gemm_bf16_decode(st, kGateUp, g1);
+            if (decode1) slices1 = launch_gemm_bf16_decode(st, kGateUp, g1);
             else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kBf16, T);
         }
         swiglu();
         g2.a = at<void>(ws, L.hbuf);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) slices = launch_gemm_bf16_decode(st, kDown, g2);
+            if (decode2) slices = launch_gemm_bf16_decode(st, kDown, g2);
             else slices = launch_tiled(st, kDown, g2, PrefillWeights::kBf16, P);
         }
     } else if (c.weight_dtype == BEAM_DTYPE_FP8_E4M3) {
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) slices1 = launch_gemm_fp8_decode(st, kGateUp, g1);
+            if (decode1) slices1 = launch_gemm_fp8_decode(st, kGateUp, g1);
             else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kFp8, T);
         }
         swiglu();
@@ -320,13 +328,13 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) slices = launch_gemm_fp8_decode(st, kDown, g2);
+            if (decode2) slices = launch_gemm_fp8_decode(st, kDown, g2);
             else slices = launch_tiled(st, kDown, g2, PrefillWeights::kFp8, P);
         }
     } else {            // MXFP4 weights
         {
             Bracket b(BEAM_KERNEL_GATE_UP, st);
-            if (decode) slices1 = launch_gemm_mxfp4_decode(st, kGateUp, g1);
+            if (decode1) slices1 = launch_gemm_mxfp4_decode(st, kGateUp, g1);
             else slices1 = launch_tiled(st, kGateUp, g1, PrefillWeights::kMxfp4, T);
         }
         swiglu();
@@ -334,7 +342,7 @@ void run_experts(const beam_moe_config& c, int64_t T, const Layout& L, void* ws,
         g2.a = at<void>(ws, L.h8); g2.a_scale = at<float>(ws, L.h8s);
         {
             Bracket b(BEAM_KERNEL_DOWN, st);
-            if (decode) slices = launch_gemm_mxfp4_decode(st, kDown, g2);
+            if (decode2) slices = launch_gemm_mxfp4_decode(st, kDown, g2);
             else slices = launch_tiled(st, kDown, g2, PrefillWeights::kMxfp4, P);
         }
     }
@@ -402,21 +410,24 @@ static int check_weights(const beam_moe_config* cfg, int64_t T, const void* w13,
     const bool scaled = cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 || cfg->weight_dtype == BEAM_DTYPE_MXFP4;
     if (scaled != (w13_scale != nullptr) || scaled != (w2_scale != nullptr)) return BEAM_ERR_INVALID_ARG;
     if (scaled && (!aligned16(w13_scale) || !aligned16(w2_scale))) return BEAM_ERR_INVALID_ARG;
-    const int64_t stream_max = dense ? kDenseStreamMaxT : kDecodeMaxT;
-    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4 && T > stream_max) {
-        // above the streaming range, MXFP4 tiles stage their weight scales in LDS; the
-        // dense MLP's down GEMM splits K into slices whose scales fit
-        if (cfg->hidden > kMxfp4PrefillMaxKd) return BEAM_ERR_UNSUPPORTED;
-        if (dense) {
+    // GEMMs above their streaming range run LDS-tiled (gate/up reduces over hidden, down
+    // over inter)
+    const bool tiled1 = T > stream_max_t(*cfg, dense, kGateUp);
+    const bool tiled2 = T > stream_max_t(*cfg, dense, kDown);
+    if (cfg->weight_dtype == BEAM_DTYPE_MXFP4) {
+        // MXFP4 tiles stage their weight scales in LDS; the dense MLP's down GEMM splits K
+        // into slices whose scales fit
+        if (tiled1 && cfg->hidden > kMxfp4PrefillMaxKd) return BEAM_ERR_UNSUPPORTED;
+        if (tiled2 && dense) {
             const int ms = dense_mxfp4_min_slices(*cfg);
             if (ms > kMaxKSplit || cfg->inter % (ms * 512) != 0) return BEAM_ERR_UNSUPPORTED;
-        } else if (cfg->inter > kMxfp4PrefillMaxKd) {
+        } else if (tiled2 && cfg->inter > kMxfp4PrefillMaxKd) {
             return BEAM_ERR_UNSUPPORTED;
         }
     }
-    // above it, FP8 tiles hold the K-block scale codes of one reduction in LDS
-    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 && T > stream_max &&
-        (cfg->hidden > kFp8PrefillMaxKd || cfg->inter > kFp8PrefillMaxKd))
+    // FP8 tiles hold the K-block scale codes of one reduction in LDS
+    if (cfg->weight_dtype == BEAM_DTYPE_FP8_E4M3 &&
+        ((tiled1 && cfg->hidden > kFp8PrefillMaxKd) || (tiled2 && cfg->inter > kFp8PrefillMaxKd)))
         return BEAM_ERR_UNSUPPORTED;
     return BEAM_OK;
 }

@@ -24,9 +24,14 @@ __host__ __device__ inline int expert_tile_first(int n, int j, int BM) {
     const int64_t m = (n + 31) / 32;
     return static_cast<int>((j * m / nt) * 32);
 }
-constexpr int kDecodeMaxT = 256;    // token counts up to this use the streaming GEMMs
-constexpr int kWideStreamMaxT = 127;   // the same with BF16 or FP8 weights (the 128-byte-stage tiled GEMM wins above)
-constexpr int kDenseStreamMaxT = 16;   // the same for the dense MLP (all rows on one weight set)
+// Token counts up to which a GEMM uses the streaming kernels (measured crossovers; the
+// LDS-tiled kernels above): MXFP4 weights, both GEMMs
+constexpr int kDecodeMaxT = 256;
+// BF16 and FP8 weights, per GEMM (the tiled down GEMM, with I = 2560 columns of
+// reduction, takes over later than the tiled gate/up GEMM)
+constexpr int kBf16GateUpStreamMaxT = 32, kBf16DownStreamMaxT = 55;
+constexpr int kFp8GateUpStreamMaxT = 16, kFp8DownStreamMaxT = 103;
+constexpr int kDenseStreamMaxT = 16;   // the dense MLP (all rows on one weight set), both GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
 // chunk sums) below 4096 tokens, where it fills the chip and the tiled kernel cannot,

@@ -127,10 +127,12 @@ def test_route_and_sublayer_argument_errors():
 
 
 def test_fp8_reduction_bound_above_the_streaming_range():
-    """FP8 tiles keep the K-block scale codes of one reduction in LDS: K <= 32768."""
+    """FP8 tiles keep the K-block scale codes of one reduction in LDS: K <= 32768 where a
+    GEMM runs tiled (the down GEMM, reducing over inter, from 104 tokens on)."""
     c = beam(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3, inter=32768 + 128)
     fwd = lambda T: bm.lib().beam_moe_forward(ctypes.byref(c), T, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
                                               FAKE, None, None, FAKE, 1 << 40, None)
+    assert fwd(104) == bm.BEAM_ERR_UNSUPPORTED
     assert fwd(257) == bm.BEAM_ERR_UNSUPPORTED
 
 

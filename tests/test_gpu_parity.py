@@ -192,8 +192,8 @@ def test_router_all_ties_and_duplicated_columns():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name,T", [("beam_decode_t16", None), ("beam_decode_t16", 1),
                                     ("beam_decode_t16", 17), ("beam_decode_t16", 32),
-                                    ("beam_prefill_t4096", 33), ("beam_prefill_t4096", 127),
-                                    ("beam_prefill_t4096", 128), ("beam_prefill_t4096", 256),
+                                    ("beam_prefill_t4096", 33), ("beam_prefill_t4096", 55),
+                                    ("beam_prefill_t4096", 56), ("beam_prefill_t4096", 256),
                                     ("beam_prefill_t4096", 257), ("beam_prefill_t4096", 1000),
                                     ("beam_prefill_t4096", None),
                                     ("beam_prefill_t4096", 4097), ("beam_skewed_t32768", None)])
@@ -271,10 +271,11 @@ def test_fp8_sublayer():
     assert e_h <= TOL[DT_FP8]
 
 
-@pytest.mark.parametrize("T", [16, 100, 200, 700])
+@pytest.mark.parametrize("T", [16, 17, 100, 104, 200, 700])
 def test_fp8_forward(T):
-    """FP8 experts through beam_moe_forward: the streaming kernels (T <= 127; 16 or 32
-    rows per pass) and the LDS-tiled kernels with mostly partial tiles (T = 200, 700)."""
+    """FP8 experts through beam_moe_forward at the crossovers: both GEMMs streaming (T =
+    16), LDS-tiled gate/up with the streaming down GEMM (17, 100), both tiled with mostly
+    partial tiles (104, 200, 700)."""
     w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192")
     from dataclasses import replace
     from beam_inputs import token_inputs, to_bf16_bits
