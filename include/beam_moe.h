@@ -30,8 +30,12 @@
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *
  * Routing contract (so that the integer result is unique and reproducible):
- *   logits   z[t,e] = fma chain over h = 0..H-1 ascending of x[t,h] * w_router[h,e],
- *            starting from 0, then + logit_bias[e] (one rounded add) when given;
+ *   logits   z[t,e]: the hidden dimension is cut into 64 contiguous chunks of H/64
+ *            entries; each chunk is one fused multiply-add chain of x[t,h] * w_router[h,e]
+ *            over its h ascending, starting from 0; the 64 chunk sums are added in
+ *            ascending chunk order (sum = 0, then sum = sum + chunk_c for c = 0..63),
+ *            then + logit_bias[e] (one rounded add) when given.  All FP32, round to
+ *            nearest even, no flush of denormals;
  *   scores   s = 1 / (1 + exp(-z)) with exp computed by Cody-Waite reduction and a
  *            degree-7 Taylor polynomial (FP32, argument clamped to [-87, 87]);
  *   order    every ranking is "larger value first, equal values -> lower index first";

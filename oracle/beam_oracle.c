@@ -9,8 +9,8 @@
  * the router.  The pages fix these sites to FP32 (Reflection Beam 1.0 overview,
  * section "Residual stream: depth-dependent weights keep the hidden state at
  * constant scale", last paragraph: the router and the norms are computed in FP32).
- * Everything else (expert MLPs, combine, post-norm, residual) is in oracle/moe.py,
- * in float64.
+ * Everything else (expert MLPs, combine, post-norm, residual) is in
+ * oracle/__init__.py, in float64 with numpy.
  *
  * Build: gcc -O3 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off -mfma -mavx2
  * (no fast-math; -ffp-contract=off so that every a*b+c not written as fmaf is two

@@ -2,12 +2,29 @@
 // The declarations and the full contract of every entry point are in beam_moe.h.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
+#include <set>
 #include <string.h>
+#include <utility>
 
 #include "beam_moe.h"
 #include "kernels.h"
 
 using namespace beam;
+
+namespace beam {
+
+void lds_opt_in(const void* kernel, int bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    static std::mutex mu;
+    static std::set<std::pair<const void*, int>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.emplace(kernel, dev).second)
+        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+}  // namespace beam
 
 namespace {
 

@@ -156,12 +156,8 @@ __global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint
 void launch_prenorm(hipStream_t st, int64_t T, int H, const uint16_t* h, const float* gain,
                     float eps, float* xhat32, uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale) {
     if (T == 0) return;
-    static bool attr_set = false;     // up to 128 KB of LDS (H <= 16384): opt in once
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prenorm_rows),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 16384);
-        attr_set = true;
-    }
+    // up to 128 KB of LDS (H <= 16384)
+    lds_opt_in(reinterpret_cast<const void*>(&prenorm_rows), 4 * 2 * 16384);
     prenorm_rows<<<static_cast<unsigned>((T + 3) / 4), 256, 4 * sizeof(uint16_t) * H, st>>>(
         T, H, h, gain, eps, xhat32, x_bf16, x_fp8, x_scale);
 }

@@ -414,12 +414,8 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
 
 template <int MODE, bool GATHER, int WT, bool SPLIT>
 static void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT, SPLIT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes_max<WT>()));
-        attr_set = true;
-    }
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT, SPLIT>),
+               static_cast<int>(lds_bytes_max<WT>()));
     const int klen = g.kd / ks;
     size_t extra = 0;
     if (WT == kWtMxfp4) extra = 256 * static_cast<size_t>(klen / 32);

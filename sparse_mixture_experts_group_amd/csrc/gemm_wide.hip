@@ -339,12 +339,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
 
 template <int MODE, bool GATHER, bool FP8, bool SPLIT>
 static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, SPLIT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kWideLds));
-        attr_set = true;
-    }
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, SPLIT>), static_cast<int>(kWideLds));
     const size_t lds = kWideLds;
     if (SPLIT) {
         GroupedGemmArgs gs = g;

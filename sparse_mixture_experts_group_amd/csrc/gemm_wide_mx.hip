@@ -276,12 +276,7 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
 
 template <int MODE, bool GATHER, bool SPLIT>
 static void launch_wide_mx_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    static bool attr_set = false;     // the LDS opt-in is per kernel, set on first use
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide_mx<MODE, GATHER, SPLIT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide_mx<MODE, GATHER, SPLIT>), 160 * 1024);
     // the pipeline's slots and scales, or the BF16 epilogue's staging if larger
     size_t lds = kMxStageLds + 256 * static_cast<size_t>(g.kd / ks / 32);
     if (!SPLIT && MODE == kDown && lds < wide_epilogue_lds(MODE)) lds = wide_epilogue_lds(MODE);

@@ -43,6 +43,10 @@ inline bool router_uses_partials(int64_t T, int H, int E) {
 
 inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
 
+// Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per
+// (kernel, device) in the process (the attribute belongs to a device).
+void lds_opt_in(const void* kernel, int bytes);
+
 enum GemmMode { kGateUp = 0, kDown = 1 };
 
 // router.hip

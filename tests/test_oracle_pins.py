@@ -551,6 +551,115 @@ def test_prenorm_closed_forms_and_order():
     assert abs(float(r1[0]) - rr) <= 1e-6 * rr
 
 
+def pin_rmsnorm_constant_vector():
+    """RMSNorm of c * 1 is sign(c) |c| / sqrt(c^2 + eps), times the gain (the mean of
+    squares of a constant vector is c^2).  eps large enough that its place matters."""
+    H, eps = 8, 0.5
+    g = np.array([2.0, 0.5, 1.0, 3.0, -1.0, 0.25, 1.5, 4.0])
+    for c in (-1.5, 0.75, 3.0):
+        got = oracle.rmsnorm64(np.full((1, H), c), g, eps)
+        want = np.sign(c) * abs(c) / math.sqrt(c * c + eps) * g
+        assert np.allclose(got[0], want, rtol=1e-14, atol=0.0), (c, got, want)
+
+
+def pin_rmsnorm_known_mean_square_per_row():
+    """Rows with hand-computed mean squares, normalised each on its own: [3, 4, 0, 0]
+    has mean square 25/4, [1, 1, 1, 1] has 1, [0, 0, 0, 2] has 1; a non-unit gain
+    multiplies the normalised value (not the input)."""
+    eps = 0.75
+    y = np.array([[3.0, 4.0, 0.0, 0.0], [1.0, 1.0, 1.0, 1.0], [0.0, 0.0, 0.0, 2.0]])
+    ms = np.array([25.0 / 4.0, 1.0, 1.0])
+    g = np.array([1.0, 2.0, -0.5, 3.0])
+    got = oracle.rmsnorm64(y, g, eps)
+    want = np.empty_like(y)
+    for t in range(3):
+        for j in range(4):
+            want[t, j] = y[t, j] / math.sqrt(ms[t] + eps) * g[j]
+    assert np.allclose(got, want, rtol=1e-14, atol=0.0)
+    # no gain = unit gain
+    assert np.allclose(oracle.rmsnorm64(y, None, eps), want / g, rtol=1e-14, atol=0.0)
+
+
+def pin_sublayer_impulse_closed_form():
+    """A residual stream with one nonzero entry per token, through experts that all hold
+    one impulse weight each (so the routing does not matter and the MoE output has one
+    nonzero entry): every step of pre-norm -> MoE -> post-norm -> residual has a closed
+    form.  h' = sqrt((k-1)/k) h + (1/sqrt k) RMSNorm(y) g_post (Beam overview,
+    "Residual stream")."""
+    H, I, E, G, Kg, K, alpha = 64, 8, 16, 4, 2, 4, 2.5
+    h0, j0, m0 = 5, 3, 41
+    a, b, d = 0.25, -0.5, 1.75
+    eps = 0.3
+    w13 = np.zeros((E, 2 * I, H), np.float32)
+    w13[:, j0, h0] = a
+    w13[:, I + j0, h0] = b
+    w2 = np.zeros((E, H, I), np.float32)
+    w2[:, m0, j0] = d
+    bank = oracle.ExpertBank(w13, w2, "f32")
+    rs = np.random.default_rng(31)
+    wr = rs.standard_normal((H, E)).astype(np.float32)
+    c_tok = np.array([1.5, -4.0, 0.25], np.float32)        # two tokens' magnitudes differ
+    h = np.zeros((3, H), np.float32)
+    h[:, h0] = c_tok
+    g_post = np.ones(H, np.float32)
+    g_post[m0] = 1.5
+    for k in (4, 10):
+        r = oracle.sublayer_forward(h, None, g_post, k, eps, wr, None, bank, G, Kg, K, alpha)
+        c1, c2 = math.sqrt((k - 1) / k), 1.0 / math.sqrt(k)
+        for t, c in enumerate(c_tok.astype(np.float64)):
+            xh = c / math.sqrt(c * c / H + eps)              # pre-norm of c e_h0 at h0
+            y = alpha * d * (a * xh) / (1.0 + math.exp(-a * xh)) * (b * xh)
+            yn = y / math.sqrt(y * y / H + eps) * 1.5        # post-norm of y e_m0 at m0
+            want = np.zeros(H)
+            want[h0] = c1 * c
+            want[m0] = c2 * yn
+            # FP32 pre-norm and FP32 combine weights: ~1e-6 relative
+            assert np.allclose(r["h_new"][t], want, rtol=2e-6, atol=1e-7), (k, t, r["h_new"][t], want)
+            assert np.allclose(r["y"][t], np.where(np.arange(H) == m0, y, 0.0), rtol=2e-6, atol=1e-7)
+
+
+POSTNORM_PINS = (pin_rmsnorm_constant_vector, pin_rmsnorm_known_mean_square_per_row,
+                 pin_sublayer_impulse_closed_form)
+
+
+@pytest.mark.parametrize("pin", POSTNORM_PINS, ids=lambda f: f.__name__)
+def test_postnorm_and_sublayer_pins(pin):
+    pin()
+
+
+def _mutant_rmsnorm(kind):
+    def f(y, gain, eps):
+        if kind == "eps_outside_sqrt":
+            r = 1.0 / (np.sqrt(np.mean(y * y, axis=1, keepdims=True)) + eps)
+        elif kind == "mean_wrong_axis":
+            r = 1.0 / np.sqrt(np.mean(y * y, axis=0, keepdims=True) + eps)
+        elif kind == "gain_before_norm":
+            y = y * (1.0 if gain is None else gain.astype(np.float64))
+            return y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+        out = y * r
+        return out if gain is None else out * gain.astype(np.float64)
+    return f
+
+
+@pytest.mark.parametrize("mistake", ["eps_outside_sqrt", "mean_wrong_axis", "gain_before_norm",
+                                     "c1_c2_swapped"])
+def test_postnorm_pins_catch_planted_mistakes(mistake, monkeypatch):
+    """Each plausible mistake in the post-norm or the residual, planted in the oracle on
+    the CPU, fails at least one of the pins above."""
+    if mistake == "c1_c2_swapped":
+        good = oracle.residual_coeffs
+        monkeypatch.setattr(oracle, "residual_coeffs", lambda k: good(k)[::-1])
+    else:
+        monkeypatch.setattr(oracle, "rmsnorm64", _mutant_rmsnorm(mistake))
+    failed = 0
+    for pin in POSTNORM_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin caught {mistake}"
+
+
 def test_residual_constant_scale_and_equal_weights():
     """c1^2 + c2^2 = 1; after steps 2..n the stream is (1/sqrt n) * (embedding + sum
     of outputs): every contribution carries the same weight (pages: 104 additions)."""
