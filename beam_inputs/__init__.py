@@ -102,22 +102,32 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quantize_e4m3_blocks(w: np.ndarray, block: int = 128):
+FP8_SCALE_KINDS = ("amax", "pow2")
+
+
+def quantize_e4m3_blocks(w: np.ndarray, block: int = 128, kind: str = "amax"):
     """Block-scaled E4M3 quantisation of a [N, K] float32 matrix.
 
-    Each block x block tile gets one power-of-two float32 scale, the smallest with
-    amax / scale <= 448 (1 for an all-zero tile), so the scale is exactly an E8M0
-    block exponent; codes = E4M3(w / scale), with amax / scale in (224, 448].
-    Returns (codes uint8 [N, K], scales float32 [N/block, K/block]).
+    Each block x block tile gets one float32 scale (1 for an all-zero tile):
+      "amax": scale = amax / 448 rounded to float32, so the tile's largest magnitude
+              maps to the top of the E4M3 range (any float32 value);
+      "pow2": the smallest power of two with amax / scale <= 448, so the scale is
+              exactly an E8M0 block exponent (amax / scale in (224, 448]).
+    codes = E4M3(w / scale), computed in float32 (round to nearest even, saturating
+    at 448).  Returns (codes uint8 [N, K], scales float32 [N/block, K/block]).
     """
+    assert kind in FP8_SCALE_KINDS, kind
     n, k = w.shape
     assert n % block == 0 and k % block == 0
     t = w.reshape(n // block, block, k // block, block)
-    amax = np.abs(t).max(axis=(1, 3)).astype(np.float64)
-    # ceil(log2(amax / 448)) from the exact binary exponent: frexp gives m in [0.5, 1)
-    m, ex = np.frexp(amax / E4M3_MAX)
-    ex = np.where(m == 0.5, ex - 1, ex)
-    scale = np.where(amax > 0, np.ldexp(1.0, ex), 1.0).astype(np.float32)
+    amax = np.abs(t).max(axis=(1, 3)).astype(np.float32)
+    if kind == "amax":
+        scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    else:
+        # ceil(log2(amax / 448)) from the exact binary exponent: frexp gives m in [0.5, 1)
+        m, ex = np.frexp(amax.astype(np.float64) / E4M3_MAX)
+        ex = np.where(m == 0.5, ex - 1, ex)
+        scale = np.where(amax > 0, np.ldexp(1.0, ex), 1.0).astype(np.float32)
     scaled = (t / scale[:, None, :, None]).astype(np.float32)
     codes = encode_e4m3(scaled).reshape(n, k)
     return codes, scale
@@ -195,6 +205,7 @@ class Workload:
     step_k: int = 10
     norm_eps: float = 1e-6
     fp8_block: int = 128
+    fp8_scales: str = "amax"       # FP8 block scales: "amax" (amax / 448) or "pow2"
     seed: int = 0
 
     def with_T(self, T: int) -> "Workload":
@@ -213,9 +224,13 @@ WORKLOADS = {
     # Beam-shaped prefill with Zipf(1.1) skewed routing
     "beam_skewed_t32768": Workload("beam_skewed_t32768", T=32768, H=5120, I=2560, E=256, G=8, Kg=4, K=8,
                                    zipf_s=1.1),
-    # full sublayer with FP8 experts
+    # full sublayer with FP8 experts (block scales amax / 448)
     "beam_sublayer_fp8_t8192": Workload("beam_sublayer_fp8_t8192", T=8192, H=5120, I=2560, E=256, G=8,
                                         Kg=4, K=8, weight_dtype=DT_FP8, sublayer=True),
+    # the same with power-of-two block scales (E8M0 block exponents)
+    "beam_sublayer_fp8pow2_t8192": Workload("beam_sublayer_fp8pow2_t8192", T=8192, H=5120, I=2560, E=256,
+                                            G=8, Kg=4, K=8, weight_dtype=DT_FP8, sublayer=True,
+                                            fp8_scales="pow2"),
     # MXFP4 experts (E2M1 elements, E8M0 scale per 32 along K): decode batch and prefill
     "beam_decode_mxfp4_t16": Workload("beam_decode_mxfp4_t16", T=16, H=5120, I=2560, E=256, G=8, Kg=4, K=8,
                                       weight_dtype=DT_MXFP4, x_recipe="rms_normal"),
@@ -331,8 +346,8 @@ def make_inputs(w: Workload, experts: list[int] | None = None) -> Inputs:
         elif w.weight_dtype == DT_BF16:
             w13[e], w2[e] = to_bf16_bits(g13), to_bf16_bits(g2)
         elif w.weight_dtype == DT_FP8:
-            w13[e], s13[e] = quantize_e4m3_blocks(g13, w.fp8_block)
-            w2[e], s2[e] = quantize_e4m3_blocks(g2, w.fp8_block)
+            w13[e], s13[e] = quantize_e4m3_blocks(g13, w.fp8_block, w.fp8_scales)
+            w2[e], s2[e] = quantize_e4m3_blocks(g2, w.fp8_block, w.fp8_scales)
         else:
             w13[e], s13[e] = quantize_mxfp4(g13)
             w2[e], s2[e] = quantize_mxfp4(g2)

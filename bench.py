@@ -91,13 +91,16 @@ class Layer:
         self.s13 = up(inp.w13_scale) if inp.w13_scale is not None else None
         self.s2 = up(inp.w2_scale) if inp.w2_scale is not None else None
         self.bias = up(inp.logit_bias) if inp.logit_bias is not None else None
+        kind = bm.BEAM_FP8_SCALES_POW2 if w.fp8_scales == "pow2" else bm.BEAM_FP8_SCALES_FP32
         if w.dense:
             self.cfg = bm.make_dense_config(hidden=w.H, inter=w.I, act_dtype=w.act_dtype,
-                                            weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+                                            weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps,
+                                            fp8_scale_kind=kind)
         else:
             self.cfg = bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg,
                                       topk=w.K, routed_scale=w.alpha, act_dtype=w.act_dtype,
-                                      weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+                                      weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps,
+                                      fp8_scale_kind=kind)
 
     def measure(self, T: int, steps: int, warmup: int) -> dict:
         """Time `steps` forwards over the first T tokens (after `warmup` untimed ones):

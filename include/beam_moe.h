@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BEAM_MOE_ABI_VERSION 3
+#define BEAM_MOE_ABI_VERSION 4
 
 typedef enum {
     BEAM_OK = 0,
@@ -64,16 +64,33 @@ typedef enum {
 typedef enum {
     BEAM_DTYPE_F32 = 0,
     BEAM_DTYPE_BF16 = 1,
-    BEAM_DTYPE_FP8_E4M3 = 2,    /* OCP E4M3FN, block-scaled (power-of-two FP32 scales) */
+    BEAM_DTYPE_FP8_E4M3 = 2,    /* OCP E4M3FN with one FP32 scale per 128 x 128 block */
     BEAM_DTYPE_MXFP4 = 3        /* OCP MX FP4 (E2M1 elements, E8M0 scale per 32 along K);
                                    weights only */
 } beam_dtype;
 
 /*
+ * What the caller guarantees about FP8 block scales (beam_moe_config.fp8_scale_kind).
+ *   BEAM_FP8_SCALES_FP32  any positive normal FP32 values, e.g. amax / 448 per block
+ *                         (the default; every kernel applies the full value)
+ *   BEAM_FP8_SCALES_POW2  every scale is a positive power of two (an E8M0 block exponent):
+ *                         the LDS-tiled GEMMs then apply only each scale's exponent field,
+ *                         through the matrix cores' block scaling, and skip the significand
+ *                         fold.  The library does not read the scales on the host to check
+ *                         this; with other scales the tiled GEMMs drop their significands.
+ * Ignored unless weight_dtype is BEAM_DTYPE_FP8_E4M3.
+ */
+typedef enum {
+    BEAM_FP8_SCALES_FP32 = 0,
+    BEAM_FP8_SCALES_POW2 = 1
+} beam_fp8_scale_kind;
+
+/*
  * Layer configuration.  Validated on every call:
  *   hidden, inter >= 1; n_experts in [2, 256]; n_groups >= 1 divides n_experts and the
  *   group size S = n_experts / n_groups is >= 2; 1 <= topk_groups <= n_groups;
- *   1 <= topk <= min(32, topk_groups * S); routed_scale finite.
+ *   1 <= topk <= min(32, topk_groups * S); routed_scale finite; fp8_scale_kind is
+ *   BEAM_FP8_SCALES_FP32 or BEAM_FP8_SCALES_POW2.
  * Kernel support (else BEAM_ERR_UNSUPPORTED):
  *   (act, weight) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (BF16, MXFP4)};
  *   hidden <= 16384; hidden and inter multiples of 64 for F32 weights; otherwise
@@ -83,7 +100,7 @@ typedef enum {
  *   Per call, where a GEMM runs LDS-tiled: MXFP4 weights above 256 tokens need
  *   hidden and inter <= 8192; FP8 weights need hidden <= 32768 above 16 tokens and
  *   inter <= 32768 above 103 tokens.
- * Beam: {5120, 2560, 256, 8, 4, 8, 2.5f, BF16, BF16 or FP8_E4M3, 128, 1e-6f}.
+ * Beam: {5120, 2560, 256, 8, 4, 8, 2.5f, BF16, BF16 or FP8_E4M3, 128, 1e-6f, FP32 scales}.
  */
 typedef struct beam_moe_config {
     int32_t hidden;        /* H */
@@ -97,6 +114,7 @@ typedef struct beam_moe_config {
     int32_t weight_dtype;  /* beam_dtype of w13 / w2 */
     int32_t fp8_block;     /* weight scale block edge for FP8 (128); ignored otherwise */
     float   norm_eps;      /* RMSNorm epsilon (sublayer only) */
+    int32_t fp8_scale_kind;  /* beam_fp8_scale_kind (FP8 weights; 0 = general FP32 scales) */
 } beam_moe_config;
 
 /* Human-readable name of a beam_status value (static string, never NULL). */
@@ -142,14 +160,13 @@ int beam_moe_route(const beam_moe_config* cfg, int64_t T, const void* x,
  *              each row H-contiguous (MXFP4: [E, 2I, H/2] bytes, element 2j of a
  *              row in the low nibble of byte j, 2j+1 in the high nibble)
  *   w13_scale  FP8: device [E, 2I/128, H/128] FP32 block scales (value = code *
- *              scale of its 128x128 tile).  Each scale must be a normal power of two
- *              (an E8M0 block exponent): in the LDS-tiled GEMMs (gate/up above 16
- *              tokens, down above 103) the matrix cores apply only its exponent field.  MXFP4: device [E, 2I, H/32] uint8 E8M0 codes
+ *              scale of its 128x128 tile), positive normal FP32 values, or powers of
+ *              two only when cfg->fp8_scale_kind says so.  MXFP4: device [E, 2I, H/32] uint8 E8M0 codes
  *              (value = E2M1 element * 2^(code - 127) of its block of 32 along K).
  *              NULL for F32 and BF16 weights.
  *   w2         device [E, H, I] weight_dtype (down projection, rows I-contiguous;
  *              MXFP4: [E, H, I/2] bytes)
- *   w2_scale   FP8: device [E, H/128, I/128] FP32 powers of two; MXFP4: [E, H, I/32]
+ *   w2_scale   FP8: device [E, H/128, I/128] FP32 (as w13_scale); MXFP4: [E, H, I/32]
  *              uint8 E8M0; NULL otherwise
  *   y          device [T, H] act_dtype out
  *   ids_out    device [T, K] int32 out, or NULL;  weights_out device [T, K] FP32 or NULL
@@ -213,8 +230,9 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
  * do not give its intermediate size):
  *   y[t] = Wd (SiLU(Wg x_t) * (Wu x_t))
  * Of cfg only hidden (H), inter (the dense intermediate size I), act_dtype,
- * weight_dtype, fp8_block and norm_eps are read (hidden, inter >= 1, dtypes in range,
- * norm_eps finite and >= 0, else BEAM_ERR_INVALID_ARG); the router fields are ignored.
+ * weight_dtype, fp8_block, norm_eps and fp8_scale_kind are read (hidden, inter >= 1,
+ * dtypes and scale kind in range, norm_eps finite and >= 0, else BEAM_ERR_INVALID_ARG);
+ * the router fields are ignored.
  * Kernel support is that of the MoE layer's expert GEMMs (dtype pairs, multiples and
  * per-call limits above), except that the streaming kernels, which read the weights
  * once per 32 rows, serve up to 16 tokens and the LDS-tiled kernels above, and that
@@ -224,7 +242,7 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
  * holds.  The weights have the layout of one expert of beam_moe_forward (E = 1):
  *   x          device [T, H] act_dtype
  *   w13        device [2I, H] weight_dtype (rows 0..I-1 gate, I..2I-1 up; MXFP4
- *              [2I, H/2] bytes);  w13_scale FP8 [2I/128, H/128] FP32 powers of two,
+ *              [2I, H/2] bytes);  w13_scale FP8 [2I/128, H/128] FP32 (as above),
  *              MXFP4 [2I, H/32] E8M0 codes, NULL otherwise
  *   w2         device [H, I] weight_dtype (MXFP4 [H, I/2]);  w2_scale FP8
  *              [H/128, I/128], MXFP4 [H, I/32], NULL otherwise

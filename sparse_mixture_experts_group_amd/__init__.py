@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libbeam_moe.so")
 
 BEAM_OK, BEAM_ERR_INVALID_ARG, BEAM_ERR_UNSUPPORTED, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = range(5)
 BEAM_DTYPE_F32, BEAM_DTYPE_BF16, BEAM_DTYPE_FP8_E4M3, BEAM_DTYPE_MXFP4 = range(4)
+BEAM_FP8_SCALES_FP32, BEAM_FP8_SCALES_POW2 = range(2)
 
 C_FUNCTIONS = ("beam_moe_status_string", "beam_moe_abi_version", "beam_moe_workspace_size",
                "beam_moe_workspace_map", "beam_moe_route", "beam_moe_forward",
@@ -30,7 +31,7 @@ class beam_moe_config(ctypes.Structure):
                 ("topk_groups", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("fp8_block", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("fp8_scale_kind", ctypes.c_int32)]
 
 
 class beam_moe_ws_map(ctypes.Structure):
@@ -46,11 +47,12 @@ class BeamMoEError(RuntimeError):
 
 def make_config(hidden=5120, inter=2560, n_experts=256, n_groups=8, topk_groups=4, topk=8,
                 routed_scale=2.5, act_dtype=BEAM_DTYPE_BF16, weight_dtype=BEAM_DTYPE_BF16,
-                fp8_block=128, norm_eps=1e-6) -> beam_moe_config:
+                fp8_block=128, norm_eps=1e-6, fp8_scale_kind=BEAM_FP8_SCALES_FP32) -> beam_moe_config:
     """Layer configuration; the defaults are Beam's (hidden 5120, 256 experts in 8 groups
-    of 32, top-4 groups, top-8 experts, intermediate 2560, scale 2.5)."""
+    of 32, top-4 groups, top-8 experts, intermediate 2560, scale 2.5).  fp8_scale_kind:
+    BEAM_FP8_SCALES_POW2 only when every FP8 block scale is a power of two."""
     return beam_moe_config(hidden, inter, n_experts, n_groups, topk_groups, topk, routed_scale,
-                           act_dtype, weight_dtype, fp8_block, norm_eps)
+                           act_dtype, weight_dtype, fp8_block, norm_eps, fp8_scale_kind)
 
 
 _lib = None
@@ -222,12 +224,12 @@ def beam_moe_sublayer_forward(cfg, h, step_k, w_router, w13, w2, pre_gain=None, 
 # dense SwiGLU MLP (the first decoder layers)
 # ---------------------------------------------------------------------------
 def make_dense_config(hidden=5120, inter=20480, act_dtype=BEAM_DTYPE_BF16, weight_dtype=BEAM_DTYPE_BF16,
-                      fp8_block=128, norm_eps=1e-6) -> beam_moe_config:
+                      fp8_block=128, norm_eps=1e-6, fp8_scale_kind=BEAM_FP8_SCALES_FP32) -> beam_moe_config:
     """Configuration of the dense MLP (only these fields are read; the router fields are
     left at their defaults).  The default width 20480 is a reading (8 x 2560), not a
     number on the pages."""
     return make_config(hidden=hidden, inter=inter, act_dtype=act_dtype, weight_dtype=weight_dtype,
-                       fp8_block=fp8_block, norm_eps=norm_eps)
+                       fp8_block=fp8_block, norm_eps=norm_eps, fp8_scale_kind=fp8_scale_kind)
 
 
 def beam_dense_workspace_size(cfg: beam_moe_config, T: int) -> int:

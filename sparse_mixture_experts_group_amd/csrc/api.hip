@@ -50,6 +50,7 @@ bool config_valid(const beam_moe_config* c) {
     if (c->act_dtype < BEAM_DTYPE_F32 || c->act_dtype > BEAM_DTYPE_FP8_E4M3) return false;
     if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_MXFP4) return false;
     if (!(c->norm_eps >= 0.0f) || !isfinite(c->norm_eps)) return false;
+    if (c->fp8_scale_kind != BEAM_FP8_SCALES_FP32 && c->fp8_scale_kind != BEAM_FP8_SCALES_POW2) return false;
     return true;
 }
 
@@ -252,6 +253,7 @@ GroupedGemmArgs base_args(const beam_moe_config& c, int64_t T, const Layout& L, 
     g.group_m = (P >= 512LL * c.n_experts) ? 4 : 2;
     g.max_active = static_cast<int>(P < c.n_experts ? P : c.n_experts);
     g.max_rows = static_cast<int>(T);     // a token picks an expert at most once
+    g.w_scale_pow2 = c.weight_dtype == BEAM_DTYPE_FP8_E4M3 && c.fp8_scale_kind == BEAM_FP8_SCALES_POW2;
     return g;
 }
 
@@ -543,6 +545,7 @@ static bool dense_config_valid(const beam_moe_config* c) {
     if (c->act_dtype < BEAM_DTYPE_F32 || c->act_dtype > BEAM_DTYPE_FP8_E4M3) return false;
     if (c->weight_dtype < BEAM_DTYPE_F32 || c->weight_dtype > BEAM_DTYPE_MXFP4) return false;
     if (!(c->norm_eps >= 0.0f) || !isfinite(c->norm_eps)) return false;
+    if (c->fp8_scale_kind != BEAM_FP8_SCALES_FP32 && c->fp8_scale_kind != BEAM_FP8_SCALES_POW2) return false;
     return true;
 }
 

@@ -82,6 +82,14 @@ __device__ __forceinline__ int first_lane(uint64_t m) {
     return __builtin_ctzll(m);
 }
 
+// A positive normal FP32 block scale s = 2^(c - 127) * m: c, its exponent field, is the
+// E8M0 code the scaled MFMAs apply to an operand, and m in [1, 2) its significand, which
+// they cannot apply.
+__device__ __forceinline__ int scale_e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xff; }
+__device__ __forceinline__ float scale_mantissa(float s) {
+    return __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
+}
+
 // FP32 -> OCP E4M3FN byte, round to nearest even, saturating (gfx950 conversion).
 __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
     uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

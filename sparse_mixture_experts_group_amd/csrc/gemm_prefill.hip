@@ -15,9 +15,12 @@
 // up accumulators of one output land in the same lane and the SwiGLU is applied in
 // registers.
 //
-// FP8: weights carry one power-of-two scale per 128 x 128 block, which the f8f6f4 MFMA
+// FP8: weights carry one FP32 scale per 128 x 128 block, whose exponent the f8f6f4 MFMA
 // applies itself as the E8M0 scale of its B operand (the FP32 scale's exponent field is
-// the E8M0 code), so the accumulation needs no per-block fold.  MXFP4: the FP4 B
+// the E8M0 code).  Power-of-two scales need nothing more; otherwise (MANT) the
+// significand m in [1, 2) of each block scale is folded by keeping the accumulators in
+// units of the current block's m: before the MFMAs of K block kb they are multiplied by
+// m[kb-1] / m[kb], after the last block by m[last].  MXFP4: the FP4 B
 // operand of a lane holds one 32-value MX block of its column, whose E8M0 scale is the
 // lane's B scale byte; the block's scales are staged in LDS once.  Activations (FP8 and
 // MXFP4 weights) are E4M3 with one FP32 scale per row, applied in the epilogue.
@@ -38,10 +41,13 @@ constexpr int kStages = 4;
 constexpr int kMxfp4MaxKd = 8192;               // LDS holds the block's 256 x kd/32 scales
 constexpr int kFp8MaxKb = kFp8PrefillMaxKd / 128;   // FP8: K blocks of a reduction
 // LDS after the stages: MXFP4 block scales (256 rows x kd/32 codes), or for FP8 with more
-// than 64 K blocks two rows of kd/128 block-scale codes
+// than 64 K blocks two rows of kd/128 block-scale codes (16-byte aligned size) followed
+// by two rows of kd/128 FP32 significand ratios
+constexpr int fp8_code_bytes(int kb_n) { return (2 * kb_n + 15) / 16 * 16; }
 template <int WT> constexpr size_t lds_bytes_max() {
     return kStages * stage_bytes<WT>() +
-           (WT == kWtMxfp4 ? 256 * (kMxfp4MaxKd / 32) : (WT == kWtFp8 ? 2 * kFp8MaxKb : 0));
+           (WT == kWtMxfp4 ? 256 * (kMxfp4MaxKd / 32)
+                           : (WT == kWtFp8 ? fp8_code_bytes(kFp8MaxKb) + 2 * sizeof(float) * kFp8MaxKb : 0));
 }
 static_assert(lds_bytes_max<kWtFp8>() <= 160 * 1024 && lds_bytes_max<kWtMxfp4>() <= 160 * 1024, "LDS budget");
 
@@ -89,8 +95,9 @@ template <> struct StageFrags<kWtMxfp4> { i32x8 a[4]; u32x4 b[4]; };
 // (row tile, column tile, slice) with the slice fastest and no XCD grouping, so
 // consecutive blocks -- which the dispatcher deals out over the XCDs in turn -- spread
 // the few tiles over the whole chip.
-template <int MODE, bool GATHER, int WT, bool SPLIT>
+template <int MODE, bool GATHER, int WT, bool MANT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
+    static_assert(WT == kWtFp8 || !MANT, "block-scale significands are an FP8 feature");
     constexpr int BM = kPrefillBM, BN = 256, MI = 4, NST = kStages;
     constexpr bool Q8 = WT != kWtBf16;                  // E4M3 activations with row scales
     constexpr int EB = Q8 ? 1 : 2;                      // bytes per activation element
@@ -162,9 +169,13 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
 
     // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l (gate-column
     // block in s_lo, up-column block in s_hi for gate/up; this wave's column block for
-    // down).  Blocks from 64 on are read from LDS (see below).
+    // down), and for MANT the significand ratio m[l-1] / m[l] (q_lo, q_hi; 1 for l = 0);
+    // m_end_* is the last block's significand.  Blocks from 64 on are read from LDS (see
+    // below).
     int s_lo = kUnitScale, s_hi = kUnitScale;
+    float q_lo = 1.0f, q_hi = 1.0f, m_end_lo = 1.0f, m_end_hi = 1.0f;
     uint8_t* fsc = smem + NST * SB;          // FP8, kd / 128 > 64: [2][kd / 128] codes
+    float* fsq = reinterpret_cast<float*>(fsc + fp8_code_bytes(klen / 128));   // then [2][kd / 128] ratios
     if constexpr (WT == kWtFp8) {
         const int kb_all = g.kd / 128, kb_n = klen / 128;     // K blocks of the row, of the slice
         const float* r_lo;
@@ -178,14 +189,26 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
             r_hi = r_lo;
         }
         const int l = min(lane, kb_n - 1);
-        s_lo = (__float_as_uint(r_lo[l]) >> 23) & 0xff;
-        s_hi = (__float_as_uint(r_hi[l]) >> 23) & 0xff;
+        s_lo = scale_e8m0(r_lo[l]);
+        s_hi = scale_e8m0(r_hi[l]);
+        if constexpr (MANT) {
+            const int lp = max(l - 1, 0);
+            q_lo = __fdiv_rn(scale_mantissa(r_lo[lp]), scale_mantissa(r_lo[l]));
+            q_hi = __fdiv_rn(scale_mantissa(r_hi[lp]), scale_mantissa(r_hi[l]));
+            m_end_lo = scale_mantissa(r_lo[kb_n - 1]);
+            m_end_hi = scale_mantissa(r_hi[kb_n - 1]);
+        }
         if (kb_n > 64) {
-            // the codes of every K block in LDS: row 0 the gate (down: wn = 0) column
-            // block, row 1 the up (down: wn = 1) block; waves 0 and 1 write them
+            // the codes (and ratios) of every K block in LDS: row 0 the gate (down: wn = 0)
+            // column block, row 1 the up (down: wn = 1) block; waves 0 and 1 write them
             if (wave < 2) {
+                // (for down, r_lo is this wave's own column block: wn = wave)
                 const float* src = (MODE == kGateUp) ? (wave == 0 ? r_lo : r_hi) : r_lo;
-                for (int i = lane; i < kb_n; i += 64) fsc[wave * kb_n + i] = (__float_as_uint(src[i]) >> 23) & 0xff;
+                for (int i = lane; i < kb_n; i += 64) {
+                    fsc[wave * kb_n + i] = static_cast<uint8_t>(scale_e8m0(src[i]));
+                    if constexpr (MANT)
+                        fsq[wave * kb_n + i] = __fdiv_rn(scale_mantissa(src[max(i - 1, 0)]), scale_mantissa(src[i]));
+                }
             }
             // complete before the pipeline: its waits count the direct-to-LDS loads alone
             __syncthreads();
@@ -285,17 +308,42 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                 }
             }
         };
-        auto mfma_stage = [&](const StageFrags<WT>& f, int kt) {
+        // even: kt is even, the first stage of a 128-wide K block (stages are 64 wide),
+        // where MANT moves the accumulators into the units of the block's significands
+        auto mfma_stage = [&](const StageFrags<WT>& f, int kt, auto even_tag) {
             if constexpr (WT == kWtFp8) {
                 const int kb = kt >> 1;                 // 128-wide K block of this stage
                 int sc_lo, sc_hi;
+                float r_lo = 1.0f, r_hi = 1.0f;
+                constexpr bool kRescale = MANT && decltype(even_tag)::value;
                 if (kb < 64) {
                     sc_lo = __builtin_amdgcn_readlane(s_lo, kb);
                     sc_hi = __builtin_amdgcn_readlane(s_hi, kb);
+                    if constexpr (kRescale) {
+                        r_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_lo), kb));
+                        r_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_hi), kb));
+                    }
                 } else {
                     const int kb_n = klen / 128;
-                    sc_lo = fsc[(MODE == kGateUp ? 0 : wn) * kb_n + kb];
+                    const int rl = (MODE == kGateUp ? 0 : wn) * kb_n + kb;
+                    sc_lo = fsc[rl];
                     sc_hi = (MODE == kGateUp) ? fsc[kb_n + kb] : sc_lo;
+                    if constexpr (kRescale) {
+                        r_lo = fsq[rl];
+                        r_hi = (MODE == kGateUp) ? fsq[kb_n + kb] : r_lo;
+                    }
+                }
+                if constexpr (kRescale) {
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        if (mi < MV) {
+#pragma unroll
+                            for (int ni = 0; ni < 4; ++ni) {
+                                const float r = (MODE == kGateUp && ni >= 2) ? r_hi : r_lo;
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= r;
+                            }
+                        }
                 }
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
@@ -308,6 +356,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                         }
                     }
             } else if constexpr (WT == kWtMxfp4) {
+                (void)even_tag;
                 if (MV > 0) {
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
@@ -323,6 +372,7 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
                 }
             } else {
                 (void)kt;
+                (void)even_tag;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -347,13 +397,13 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         // between them.  Unrolled by two so the fragment buffers alternate statically; the
         // body is branch-free: past the end the slab index is clamped and the last
         // iterations re-load the last slab into slots nothing reads any more.
-        auto iteration = [&](StageFrags<WT>& cur, StageFrags<WT>& nxt, int j, int slot) {
+        auto iteration = [&](StageFrags<WT>& cur, StageFrags<WT>& nxt, int j, int slot, auto even_tag) {
             const int nslot = (slot + 1 == NST) ? 0 : slot + 1;
             __builtin_amdgcn_sched_barrier(0);
             wait_lds_dma<(NST - 2) * PER>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            mfma_stage(cur, j);
+            mfma_stage(cur, j, even_tag);
             load_frags(nxt, nslot);
             dma(slot, min(j + NST, nk - 1));
             sched_interleave<NM, NR, PER>();
@@ -362,11 +412,22 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
         };
         int slot = 0;
         for (int j = 0; j < nk; j += 2) {
-            slot = iteration(f0, f1, j, slot);
-            slot = iteration(f1, f0, j + 1, slot);
+            slot = iteration(f0, f1, j, slot, std::true_type{});
+            slot = iteration(f1, f0, j + 1, slot, std::false_type{});
         }
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
+    if constexpr (MANT) {
+        // from the units of the last block's significand back to the block scales
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const float m = (MODE == kGateUp && ni >= 2) ? m_end_hi : m_end_lo;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= m;
+            }
+    }
 
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
@@ -412,39 +473,40 @@ __global__ __launch_bounds__(256) void gemm_prefill(GroupedGemmArgs g) {
     }
 }
 
-template <int MODE, bool GATHER, int WT, bool SPLIT>
+template <int MODE, bool GATHER, int WT, bool MANT, bool SPLIT>
 static void launch_prefill_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    lds_opt_in(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT, SPLIT>),
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_prefill<MODE, GATHER, WT, MANT, SPLIT>),
                static_cast<int>(lds_bytes_max<WT>()));
     const int klen = g.kd / ks;
     size_t extra = 0;
     if (WT == kWtMxfp4) extra = 256 * static_cast<size_t>(klen / 32);
-    if (WT == kWtFp8 && klen / 128 > 64) extra = 2 * static_cast<size_t>(klen / 128);
+    if (WT == kWtFp8 && klen / 128 > 64)
+        extra = fp8_code_bytes(klen / 128) + (MANT ? 2 * sizeof(float) * static_cast<size_t>(klen / 128) : 0);
     const size_t lds = kStages * stage_bytes<WT>() + extra;
     if (SPLIT) {
         GroupedGemmArgs gs = g;
         gs.k_slices = ks;
-        gemm_prefill<MODE, GATHER, WT, SPLIT><<<blocks, 256, lds, st>>>(gs);
+        gemm_prefill<MODE, GATHER, WT, MANT, SPLIT><<<blocks, 256, lds, st>>>(gs);
     } else {
-        gemm_prefill<MODE, GATHER, WT, SPLIT><<<blocks, 256, lds, st>>>(g);
+        gemm_prefill<MODE, GATHER, WT, MANT, SPLIT><<<blocks, 256, lds, st>>>(g);
     }
 }
 
-template <int WT>
+template <int WT, bool MANT>
 static void launch_prefill_dtype(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks, int ks) {
     // split K only for a single weight set (rows in token order, no gather); the grid
     // enumerates every (row tile bound, column tile, slice)
     if (ks > 1) {
         const int ncol = (mode == kGateUp) ? 128 : 256;
         const int nb = g.max_tiles * (g.n_out / ncol) * ks;
-        if (mode == kGateUp) launch_prefill_inst<kGateUp, false, WT, true>(st, g, nb, ks);
-        else launch_prefill_inst<kDown, false, WT, true>(st, g, nb, ks);
+        if (mode == kGateUp) launch_prefill_inst<kGateUp, false, WT, MANT, true>(st, g, nb, ks);
+        else launch_prefill_inst<kDown, false, WT, MANT, true>(st, g, nb, ks);
     } else if (mode == kGateUp) {
-        if (g.gather) launch_prefill_inst<kGateUp, true, WT, false>(st, g, blocks, 1);
-        else launch_prefill_inst<kGateUp, false, WT, false>(st, g, blocks, 1);
+        if (g.gather) launch_prefill_inst<kGateUp, true, WT, MANT, false>(st, g, blocks, 1);
+        else launch_prefill_inst<kGateUp, false, WT, MANT, false>(st, g, blocks, 1);
     } else {
-        if (g.gather) launch_prefill_inst<kDown, true, WT, false>(st, g, blocks, 1);
-        else launch_prefill_inst<kDown, false, WT, false>(st, g, blocks, 1);
+        if (g.gather) launch_prefill_inst<kDown, true, WT, MANT, false>(st, g, blocks, 1);
+        else launch_prefill_inst<kDown, false, WT, MANT, false>(st, g, blocks, 1);
     }
 }
 
@@ -466,9 +528,10 @@ int launch_gemm_prefill(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g,
     const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
     const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
     const int ks = prefill_k_split(mode, g, wt);
-    if (wt == PrefillWeights::kFp8) launch_prefill_dtype<kWtFp8>(st, mode, g, blocks, ks);
-    else if (wt == PrefillWeights::kMxfp4) launch_prefill_dtype<kWtMxfp4>(st, mode, g, blocks, ks);
-    else launch_prefill_dtype<kWtBf16>(st, mode, g, blocks, ks);
+    if (wt == PrefillWeights::kFp8 && g.w_scale_pow2) launch_prefill_dtype<kWtFp8, false>(st, mode, g, blocks, ks);
+    else if (wt == PrefillWeights::kFp8) launch_prefill_dtype<kWtFp8, true>(st, mode, g, blocks, ks);
+    else if (wt == PrefillWeights::kMxfp4) launch_prefill_dtype<kWtMxfp4, false>(st, mode, g, blocks, ks);
+    else launch_prefill_dtype<kWtBf16, false>(st, mode, g, blocks, ks);
     return ks;
 }
 

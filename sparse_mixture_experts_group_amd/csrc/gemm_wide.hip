@@ -1,5 +1,5 @@
-// Grouped expert GEMMs for many rows per expert with BF16 or FP8 (OCP E4M3FN, 128 x 128
-// power-of-two block scales, E4M3 activations with row scales) weights: LDS-tiled MFMA
+// Grouped expert GEMMs for many rows per expert with BF16 or FP8 (OCP E4M3FN, one FP32
+// scale per 128 x 128 block, E4M3 activations with row scales) weights: LDS-tiled MFMA
 // GEMM whose K stages hold 128 bytes of every operand row.
 //
 // SwiGLU expert (Reflection Beam 1.0 overview, "Mixture of Experts: 256 experts, 8
@@ -83,12 +83,18 @@ template <> struct StepFrags<true> { i32x8 a[4]; i32x8 b[4]; };
 // meets the others, then runs the last step's MFMAs while reading stage kt + 1's first
 // fragments and loading the activations of stage kt + 2 into the slot stage kt drained.
 // FP8: one 128 x 128 scale block per stage, at most 64 per reduction (a lane of a
-// register each).
+// register each).  The scaled MFMA applies the exponent of the block's FP32 scale (its
+// E8M0 code) to the weights.  MANT (scales that are not all powers of two): the
+// significand m in [1, 2) of each block scale is folded on the vector ALU by keeping the
+// accumulators in units of the current block's m -- before the MFMAs of K block kb they
+// are multiplied by m[kb-1] / m[kb] (1 for the first block), after the last block by
+// m[last] -- one multiply per accumulator and stage, no second set of accumulators.
 //
 // SPLIT: as in gemm_prefill.hip, the GEMMs of a single weight set split K into
 // g.k_slices slices (FP32 partial sums) over a flat block order.
-template <int MODE, bool GATHER, bool FP8, bool SPLIT>
+template <int MODE, bool GATHER, bool FP8, bool MANT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
+    static_assert(FP8 || !MANT, "block-scale significands are an FP8 feature");
     constexpr int BM = kPrefillBM, BN = 256, MI = 4, NI = 4;
     constexpr int EB = FP8 ? 1 : 2;                     // bytes per element (A and B)
     constexpr int BK = kWideRowBytes / EB;              // K per stage
@@ -157,8 +163,10 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
 
     // FP8 weight-scale exponents: lane l holds the E8M0 code of K block l of the slice
     // (gate-column block in s_lo, up-column block in s_hi for gate/up; this wave's column
-    // block for down).
+    // block for down).  MANT: lane l also holds the ratio m[l-1] / m[l] of the blocks'
+    // significands (q_lo, q_hi; 1 for l = 0), and m_end_* is the last block's.
     int s_lo = kUnitScale, s_hi = kUnitScale;
+    float q_lo = 1.0f, q_hi = 1.0f, m_end_lo = 1.0f, m_end_hi = 1.0f;
     if constexpr (FP8) {
         const int kb_all = g.kd / 128, kb_n = klen / 128;
         const float* wsc = static_cast<const float*>(g.w_scale) + kbeg / 128;
@@ -172,8 +180,15 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             r_hi = r_lo;
         }
         const int l = min(lane, kb_n - 1);
-        s_lo = (__float_as_uint(r_lo[l]) >> 23) & 0xff;
-        s_hi = (__float_as_uint(r_hi[l]) >> 23) & 0xff;
+        s_lo = scale_e8m0(r_lo[l]);
+        s_hi = scale_e8m0(r_hi[l]);
+        if constexpr (MANT) {
+            const int lp = max(l - 1, 0);
+            q_lo = __fdiv_rn(scale_mantissa(r_lo[lp]), scale_mantissa(r_lo[l]));
+            q_hi = __fdiv_rn(scale_mantissa(r_hi[lp]), scale_mantissa(r_hi[l]));
+            m_end_lo = scale_mantissa(r_lo[kb_n - 1]);
+            m_end_hi = scale_mantissa(r_hi[kb_n - 1]);
+        }
     }
 
     f32x16 acc[MI][NI];
@@ -249,11 +264,28 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                 }
             }
         };
-        auto mfma_step = [&](const StepFrags<FP8>& f, int kt) {
+        // first: the stage's first K step, where MANT moves the accumulators into the units
+        // of this stage's block-scale significands
+        auto mfma_step = [&](const StepFrags<FP8>& f, int kt, auto first_tag) {
             if constexpr (FP8) {
                 // the stage's 128-wide K block is kt (< 64)
                 const int sc_lo = __builtin_amdgcn_readlane(s_lo, kt);
                 const int sc_hi = __builtin_amdgcn_readlane(s_hi, kt);
+                if constexpr (MANT && decltype(first_tag)::value) {
+                    // into the units of this block's significands
+                    const float r_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_lo), kt));
+                    const float r_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_hi), kt));
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        if (mi < MV) {
+#pragma unroll
+                            for (int ni = 0; ni < NI; ++ni) {
+                                const float r = (MODE == kGateUp && ni >= 2) ? r_hi : r_lo;
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= r;
+                            }
+                        }
+                }
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
                     if (mi < MV) {
@@ -266,6 +298,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                     }
             } else {
                 (void)kt;
+                (void)first_tag;
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
                     if (mi < MV) {
@@ -305,7 +338,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                 StepFrags<FP8>& cur = (s & 1) ? f1 : f0;
                 StepFrags<FP8>& nxt = (s & 1) ? f0 : f1;
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_step(cur, kt);
+                mfma_step(cur, kt, std::integral_constant<bool, s == 0>{});
                 load_frags(nxt, aslot, bslot, s + 1);
                 dma_b(bfree, min(kt + 2, nk - 1), std::integral_constant<int, j0>{}, std::integral_constant<int, j1>{});
                 sched_reads_then_loads<NM, NR, j1 - j0>();
@@ -316,7 +349,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             wait_lds_dma<8>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            mfma_step(f1, kt);
+            mfma_step(f1, kt, std::false_type{});
             load_frags(f0, aslot ^ 1, bnext, 0);
             dma_a(aslot, min(kt + 2, nk - 1));           // into the slot stage kt drained
             sched_reads_then_loads<NM, NR, 2 * MV>();
@@ -326,6 +359,17 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         wait_lds_dma<0>();      // the tail's re-loads land before the block's LDS is released
     };
     dispatch_row_tiles<MI>(mvalid, k_loop);
+    if constexpr (MANT) {
+        // from the units of the last block's significand back to the block scales
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const float m = (MODE == kGateUp && ni >= 2) ? m_end_hi : m_end_lo;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= m;
+            }
+    }
 
     // down: 256-byte row segments per wave, staged through LDS for whole-row stores;
     // gate/up (128-byte segments) and FP32 partial sums: stored from the registers
@@ -337,34 +381,34 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     }
 }
 
-template <int MODE, bool GATHER, bool FP8, bool SPLIT>
+template <int MODE, bool GATHER, bool FP8, bool MANT, bool SPLIT>
 static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, SPLIT>), static_cast<int>(kWideLds));
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, MANT, SPLIT>), static_cast<int>(kWideLds));
     const size_t lds = kWideLds;
     if (SPLIT) {
         GroupedGemmArgs gs = g;
         gs.k_slices = ks;
-        gemm_wide<MODE, GATHER, FP8, SPLIT><<<blocks, 256, lds, st>>>(gs);
+        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT><<<blocks, 256, lds, st>>>(gs);
     } else {
-        gemm_wide<MODE, GATHER, FP8, SPLIT><<<blocks, 256, lds, st>>>(g);
+        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT><<<blocks, 256, lds, st>>>(g);
     }
 }
 
-template <bool FP8>
+template <bool FP8, bool MANT>
 static void launch_wide_modes(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, int blocks, int ks) {
     // split K only for a single weight set (rows in token order, no gather); the grid
     // enumerates every (row tile bound, column tile, slice)
     if (ks > 1) {
         const int ncol = (mode == kGateUp) ? 128 : 256;
         const int nb = g.max_tiles * (g.n_out / ncol) * ks;
-        if (mode == kGateUp) launch_wide_inst<kGateUp, false, FP8, true>(st, g, nb, ks);
-        else launch_wide_inst<kDown, false, FP8, true>(st, g, nb, ks);
+        if (mode == kGateUp) launch_wide_inst<kGateUp, false, FP8, MANT, true>(st, g, nb, ks);
+        else launch_wide_inst<kDown, false, FP8, MANT, true>(st, g, nb, ks);
     } else if (mode == kGateUp) {
-        if (g.gather) launch_wide_inst<kGateUp, true, FP8, false>(st, g, blocks, 1);
-        else launch_wide_inst<kGateUp, false, FP8, false>(st, g, blocks, 1);
+        if (g.gather) launch_wide_inst<kGateUp, true, FP8, MANT, false>(st, g, blocks, 1);
+        else launch_wide_inst<kGateUp, false, FP8, MANT, false>(st, g, blocks, 1);
     } else {
-        if (g.gather) launch_wide_inst<kDown, true, FP8, false>(st, g, blocks, 1);
-        else launch_wide_inst<kDown, false, FP8, false>(st, g, blocks, 1);
+        if (g.gather) launch_wide_inst<kDown, true, FP8, MANT, false>(st, g, blocks, 1);
+        else launch_wide_inst<kDown, false, FP8, MANT, false>(st, g, blocks, 1);
     }
 }
 
@@ -375,8 +419,9 @@ int launch_gemm_wide(hipStream_t st, GemmMode mode, const GroupedGemmArgs& g, bo
     const int64_t groups = (g.max_tiles + g.group_m - 1) / g.group_m;
     const int blocks = static_cast<int>((groups * g.group_m * (g.n_out / ncol) + 255) / 256 * 256);
     const int ks = prefill_k_split(mode, g, fp8 ? PrefillWeights::kFp8 : PrefillWeights::kBf16);
-    if (fp8) launch_wide_modes<true>(st, mode, g, blocks, ks);
-    else launch_wide_modes<false>(st, mode, g, blocks, ks);
+    if (!fp8) launch_wide_modes<false, false>(st, mode, g, blocks, ks);
+    else if (g.w_scale_pow2) launch_wide_modes<true, false>(st, mode, g, blocks, ks);
+    else launch_wide_modes<true, true>(st, mode, g, blocks, ks);
     return ks;
 }
 

@@ -78,6 +78,8 @@ struct GroupedGemmArgs {
     const float* a_scale;     // FP8: [rows or T, Kd/128] activation scales, else null
     const void* w;            // [E, Nw, Kd] expert weights
     const void* w_scale;      // FP8: FP32 [E, Nw/128, Kd/128]; MXFP4: E8M0 bytes [E, Nw, Kd/32]; else null
+    bool w_scale_pow2;        // FP8: every block scale is a power of two (the LDS-tiled GEMMs
+                              // then apply only its exponent, with no significand fold)
     int n_out;                // output columns (I for gate/up, H for down)
     int kd;                   // reduction length
     const int32_t* exp_cnt;   // [E]

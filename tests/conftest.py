@@ -32,7 +32,7 @@ def gpu_inputs(name: str, T: int | None = None, **overrides):
     w = WORKLOADS[name] if T is None else WORKLOADS[name].with_T(T)
     if overrides:
         w = replace(w, **overrides)
-    key_w = (w.H, w.I, w.E, w.weight_dtype, w.seed, w.dense)
+    key_w = (w.H, w.I, w.E, w.weight_dtype, w.seed, w.dense, w.fp8_scales if w.weight_dtype == 2 else None)
     if key_w not in _CACHE:
         print(f"[inputs] generating weights for {name} ...", flush=True)
         full = make_inputs(w)

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = bm.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert bm.abi_version() == 3
+    assert bm.abi_version() == 4
 
 
 def test_status_strings():
@@ -57,7 +57,7 @@ def test_workspace_size_and_map():
 @pytest.mark.parametrize("kw", [dict(n_groups=3), dict(n_groups=256), dict(topk_groups=9), dict(topk=0),
                                 dict(topk=33), dict(topk_groups=1, topk=33), dict(n_experts=512),
                                 dict(n_experts=1), dict(hidden=0), dict(routed_scale=float("nan")),
-                                dict(act_dtype=7)])
+                                dict(act_dtype=7), dict(fp8_scale_kind=2), dict(fp8_scale_kind=-1)])
 def test_invalid_config_rejected(kw):
     c = beam(**kw)
     st = bm.lib().beam_moe_forward(ctypes.byref(c), 16, FAKE, FAKE, None, None, FAKE, None, FAKE, None, FAKE,
@@ -159,6 +159,7 @@ def test_dense_workspace_and_config_checks():
 @pytest.mark.parametrize("kw,status", [(dict(hidden=0), bm.BEAM_ERR_INVALID_ARG),
                                        (dict(act_dtype=9), bm.BEAM_ERR_INVALID_ARG),
                                        (dict(norm_eps=float("inf")), bm.BEAM_ERR_INVALID_ARG),
+                                       (dict(fp8_scale_kind=5), bm.BEAM_ERR_INVALID_ARG),
                                        (dict(hidden=384), bm.BEAM_ERR_UNSUPPORTED),
                                        (dict(inter=100), bm.BEAM_ERR_UNSUPPORTED),
                                        (dict(act_dtype=bm.BEAM_DTYPE_F32), bm.BEAM_ERR_UNSUPPORTED)])

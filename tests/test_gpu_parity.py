@@ -19,10 +19,18 @@ pytestmark = pytest.mark.gpu
 TOL = {DT_F32: 1e-5, DT_BF16: 2e-2, DT_FP8: 6e-2, DT_MXFP4: 6e-2}
 
 
-def cfg_of(w):
+def scale_kind(w, declared=None):
+    """The FP8 scale kind the config declares: what the inputs hold, unless a test
+    declares general FP32 scales for power-of-two inputs."""
+    if declared is not None:
+        return declared
+    return bm.BEAM_FP8_SCALES_POW2 if w.fp8_scales == "pow2" else bm.BEAM_FP8_SCALES_FP32
+
+
+def cfg_of(w, declared=None):
     return bm.make_config(hidden=w.H, inter=w.I, n_experts=w.E, n_groups=w.G, topk_groups=w.Kg, topk=w.K,
                           routed_scale=w.alpha, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
-                          fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+                          fp8_block=w.fp8_block, norm_eps=w.norm_eps, fp8_scale_kind=scale_kind(w, declared))
 
 
 def to_dev_x(w, x):
@@ -55,8 +63,8 @@ def sample_tokens(T, n=16, seed=1):
     return np.array(sorted(base | set(int(t) for t in extra)))[:max(n, 3)]
 
 
-def run_forward(w, dev, x, bias, select_bias=None):
-    cfg = cfg_of(w)
+def run_forward(w, dev, x, bias, select_bias=None, declared=None):
+    cfg = cfg_of(w, declared)
     xd = to_dev_x(w, x)
     ids = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
     wts = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
@@ -247,9 +255,12 @@ def test_beam_bf16_intermediates_and_determinism():
 # ---------------------------------------------------------------------------
 # FP8 sublayer
 # ---------------------------------------------------------------------------
-def test_fp8_sublayer():
-    w, full, dev, x, bias = gpu_inputs("beam_sublayer_fp8_t8192")
-    print(f"[case] sublayer fp8 T={w.T}", flush=True)
+@pytest.mark.parametrize("name", ["beam_sublayer_fp8_t8192", "beam_sublayer_fp8pow2_t8192"])
+def test_fp8_sublayer(name):
+    """The FP8 sublayer at 8192 tokens with amax / 448 block scales (the significand fold
+    in the tiled GEMMs) and with power-of-two scales (exponents only)."""
+    w, full, dev, x, bias = gpu_inputs(name)
+    print(f"[case] sublayer fp8 {w.fp8_scales} T={w.T}", flush=True)
     cfg = cfg_of(w)
     h = to_dev_x(w, x)
     moe_out = torch.empty_like(h)
@@ -266,23 +277,26 @@ def test_fp8_sublayer():
     check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
     e_moe = rel_inf(moe_out.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
     e_h = rel_inf(h.float().cpu().numpy()[tok].astype(np.float64), ref["h_new"])
-    print(f"[case] sublayer fp8 moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e}", flush=True)
+    print(f"[case] sublayer fp8 {w.fp8_scales} moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e}", flush=True)
     assert e_moe <= TOL[DT_FP8]
     assert e_h <= TOL[DT_FP8]
 
 
+@pytest.mark.parametrize("scales,declared", [("amax", None), ("pow2", None),
+                                             ("pow2", bm.BEAM_FP8_SCALES_FP32)])
 @pytest.mark.parametrize("T", [16, 17, 100, 104, 200, 700])
-def test_fp8_forward(T):
+def test_fp8_forward(T, scales, declared):
     """FP8 experts through beam_moe_forward at the crossovers: both GEMMs streaming (T =
     16), LDS-tiled gate/up with the streaming down GEMM (17, 100), both tiled with mostly
-    partial tiles (104, 200, 700)."""
-    w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192")
+    partial tiles (104, 200, 700); amax / 448 block scales, power-of-two scales declared
+    as such, and power-of-two scales through the general path."""
+    w0, full, dev, _, bias = gpu_inputs("beam_sublayer_fp8_t8192", fp8_scales=scales)
     from dataclasses import replace
     from beam_inputs import token_inputs, to_bf16_bits
     w = replace(w0, T=T, sublayer=False, x_recipe="rms_normal")
     x = to_bf16_bits(token_inputs(w))
-    print(f"[case] fp8 forward T={T}", flush=True)
-    cfg, y, ids, wts, ws = run_forward(w, dev, x, None)
+    print(f"[case] fp8 forward {scales} declared={declared} T={T}", flush=True)
+    cfg, y, ids, wts, ws = run_forward(w, dev, x, None, declared=declared)
     x32 = oracle.bf16_to_f32(x)
     z = oracle.router_logits(x32, full.w_router, None)
     rid, rw = oracle.route(z, w.G, w.Kg, w.K, w.alpha)
@@ -291,7 +305,7 @@ def test_fp8_forward(T):
     tok = np.arange(T) if T <= 300 else sample_tokens(T)
     yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
     err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
-    print(f"[case] fp8 forward T={T} rel_inf={err:.3e}", flush=True)
+    print(f"[case] fp8 forward {scales} T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[DT_FP8]
 
 
@@ -329,7 +343,7 @@ _DENSE_BANK = {}
 
 def dense_bank(w, full):
     """Float64 weights of the dense MLP, decoded once per weight dtype."""
-    key = w.weight_dtype
+    key = (w.weight_dtype, w.fp8_scales)
     if key not in _DENSE_BANK:
         w13, w2 = bank_of(w, full).expert(0)
         _DENSE_BANK[key] = oracle.ExpertBank(w13[None], w2[None], "f32")
@@ -338,19 +352,23 @@ def dense_bank(w, full):
 
 def dense_cfg(w):
     return bm.make_dense_config(hidden=w.H, inter=w.I, act_dtype=w.act_dtype, weight_dtype=w.weight_dtype,
-                                fp8_block=w.fp8_block, norm_eps=w.norm_eps)
+                                fp8_block=w.fp8_block, norm_eps=w.norm_eps, fp8_scale_kind=scale_kind(w))
 
 
 @pytest.mark.parametrize("dt,T", [(DT_BF16, 16), (DT_BF16, 1), (DT_BF16, 17), (DT_BF16, 32), (DT_BF16, 33), (DT_BF16, 200),
                                   (DT_BF16, 700), (DT_BF16, 4096), (DT_FP8, 16), (DT_FP8, 200), (DT_FP8, 700),
+                                  ("fp8_pow2", 200), ("fp8_pow2", 700),
                                   (DT_MXFP4, 16), (DT_MXFP4, 32), (DT_MXFP4, 200), (DT_MXFP4, 4096)])
 def test_dense_forward(dt, T):
     """Dense MLP through beam_dense_forward: streaming kernels with both GEMMs split
     over K (T <= 16) and the LDS-tiled kernels, split over K while their tiles are few
     (T = 32, 33, 200, 700 ragged, 4096), against the oracle (every token up to 300, else
-    sampled tokens)."""
-    w, full, dev, x, _ = gpu_inputs("beam_dense_decode_t16", T, weight_dtype=dt)
-    print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T}", flush=True)
+    sampled tokens).  FP8 block scales amax / 448, or powers of two ("fp8_pow2")."""
+    scales = "amax"
+    if dt == "fp8_pow2":
+        dt, scales = DT_FP8, "pow2"
+    w, full, dev, x, _ = gpu_inputs("beam_dense_decode_t16", T, weight_dtype=dt, fp8_scales=scales)
+    print(f"[case] dense forward {DTYPE_NAMES[dt]} {scales} T={T}", flush=True)
     cfg = dense_cfg(w)
     y = bm.beam_dense_forward(cfg, to_dev_x(w, x), dev["w13"], dev["w2"], w13_scale=dev.get("w13_scale"),
                               w2_scale=dev.get("w2_scale"))
@@ -406,6 +424,8 @@ _EDGE = {
     # block scales in LDS): gate/up over H = 8448, down over I = 8448
     "fp8_long_hidden": dict(H=8448, I=256, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8),
     "fp8_long_inter": dict(H=256, I=8448, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8),
+    "fp8_long_hidden_pow2": dict(H=8448, I=256, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8, fp8_scales="pow2"),
+    "fp8_long_inter_pow2": dict(H=256, I=8448, E=16, G=4, Kg=2, K=4, weight_dtype=DT_FP8, fp8_scales="pow2"),
     # MXFP4 K slices longer than 6144 (the 64-byte-stage GEMM)
     "mxfp4_long_hidden": dict(H=6656, I=512, E=16, G=4, Kg=2, K=4, weight_dtype=DT_MXFP4),
     "mxfp4_long_inter": dict(H=512, I=6656, E=16, G=4, Kg=2, K=4, weight_dtype=DT_MXFP4),
@@ -418,7 +438,8 @@ _EDGE = {
 @pytest.mark.parametrize("case,T", [("max_hidden_topk", 16), ("max_hidden_topk", 300), ("single_group", 100),
                                     ("single_group", 700), ("all_groups_kept", 64), ("k1", 50),
                                     ("two_experts", 40), ("short_chunks", 4096), ("short_chunks", 16384),
-                                    ("fp8_long_hidden", 300), ("fp8_long_inter", 300), ("mxfp4_long_hidden", 300),
+                                    ("fp8_long_hidden", 300), ("fp8_long_inter", 300), ("fp8_long_hidden_pow2", 300),
+                                    ("fp8_long_inter_pow2", 300), ("mxfp4_long_hidden", 300),
                                     ("mxfp4_long_inter", 300), ("rows_past_4gb", 32768)])
 def test_config_limits_and_degenerate_routing(case, T):
     from beam_inputs import Workload, make_inputs

@@ -31,10 +31,40 @@ def test_e4m3_encoding_matches_torch_rne_saturating():
     assert np.array_equal(oracle.e4m3_to_f64(rt), oracle.e4m3_to_f64(codes))
 
 
+def test_block_quantisation_amax_scales():
+    """amax / 448 block scales (the plain reading of FP32 block scales): each tile's
+    largest magnitude maps onto the E4M3 maximum, 448, and the stored values are within
+    half an E4M3 step of the weights."""
+    w = normal(0, (5,), (256, 384), std=0.02)
+    w[128:, 256:] = 0.0                                   # an all-zero block
+    codes, scales = quantize_e4m3_blocks(w, 128, "amax")
+    assert scales.shape == (2, 3) and scales.dtype == np.float32
+    assert scales[1, 2] == 1.0
+    deq = oracle.dequant_blocks(codes, scales, 128)
+    m, _ = np.frexp(scales[:1].astype(np.float64))
+    assert not np.all(m == 0.5)                           # not merely powers of two
+    for i in range(2):
+        for j in range(3):
+            if i == 1 and j == 2:
+                continue
+            t = w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            amax = np.abs(t).max()
+            assert scales[i, j] == np.float32(amax) / np.float32(448.0)
+            c = codes[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            assert (np.abs(oracle.e4m3_to_f64(c)) == 448.0).any()        # the amax element
+            d = deq[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            # |w| / scale in a binade [2^e, 2^(e+1)) has step 2^(e-3): error <= step / 2
+            q = np.abs(t).astype(np.float64) / float(scales[i, j])
+            e = np.floor(np.log2(np.maximum(q, 2.0 ** -6))).astype(np.int64)
+            step = np.ldexp(1.0, e - 3)
+            assert np.all(np.abs(d - t) <= step / 2 * scales[i, j] * (1 + 1e-6) + 1e-12)
+    assert np.all(deq[128:, 256:] == 0.0)
+
+
 def test_block_quantisation_power_of_two_scales():
     w = normal(0, (5,), (256, 384), std=0.02)
     w[128:, 256:] = 0.0                                   # an all-zero block
-    codes, scales = quantize_e4m3_blocks(w, 128)
+    codes, scales = quantize_e4m3_blocks(w, 128, "pow2")
     assert scales.shape == (2, 3)
     m, _ = np.frexp(scales.astype(np.float64))
     assert np.all(m == 0.5)                               # exact powers of two (E8M0)
