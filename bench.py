@@ -9,9 +9,12 @@ down GEMM, combine) -- or `beam_moe_sublayer_forward` for the sublayer workload,
 Beam-shaped inputs already resident in HBM.  Prints ONE JSON line on stdout; progress
 goes to stderr.
 
-Default workload: the Beam-shaped decode batch (T = 16 tokens, hidden 5120, 256 experts
-in 8 groups of 32, top-4 groups, top-8, SwiGLU intermediate 2560, BF16 experts), where
-the layer streams the weights of every routed expert from HBM.
+Default workload: the Beam-shaped layer (hidden 5120, 256 experts in 8 groups of 32,
+top-4 groups, top-8, SwiGLU intermediate 2560, BF16 experts) at 32768 tokens with skewed
+routing (Zipf(1.1) logit offsets over a random expert permutation), the largest
+configuration on one GPU, where the expert GEMMs are bound by the matrix cores.  The
+same run times the decode batch (16 tokens, x RMS-normalised, the same weights), which
+streams the weights of every routed expert from HBM, and carries it in `extra`.
 """
 from __future__ import annotations
 
@@ -43,7 +46,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="beam_decode_t16")
+    p.add_argument("--workload", default="beam_skewed_t32768")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode-batch measurement carried in `extra` of the default line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--sweep", default="", metavar="T1,T2,...",
@@ -102,13 +107,16 @@ class Layer:
                                       weight_dtype=w.weight_dtype, fp8_block=w.fp8_block, norm_eps=w.norm_eps,
                                       fp8_scale_kind=kind)
 
-    def measure(self, T: int, steps: int, warmup: int) -> dict:
+    def measure(self, T: int, steps: int, warmup: int, x_rows=None, bias="layer") -> dict:
         """Time `steps` forwards over the first T tokens (after `warmup` untimed ones):
         step time from HIP events and the wall clock, the gate/up GEMM's duration from
-        events the library records around it, then the other kernels in separate passes."""
+        events the library records around it, then the other kernels in separate passes.
+        x_rows: other activations [T, H] (device) in place of the workload's; bias: the
+        logit offsets to use ("layer": the workload's)."""
         import torch
         bm, w = self.bm, self.w
-        x = self.x_all[:T].contiguous()
+        x = (self.x_all[:T] if x_rows is None else x_rows).contiguous()
+        lbias = self.bias if isinstance(bias, str) else bias
         ws = (bm.alloc_dense_workspace if w.dense else bm.alloc_workspace)(self.cfg, T, self.dev)
         ids = torch.empty((T, w.K), dtype=torch.int32, device=self.dev)
         wts = torch.empty((T, w.K), dtype=torch.float32, device=self.dev)
@@ -124,10 +132,10 @@ class Layer:
                                       ws=ws)
             elif w.sublayer:
                 bm.beam_moe_sublayer_forward(self.cfg, h, w.step_k, self.wr, self.w13, self.w2,
-                                             logit_bias=self.bias, w13_scale=self.s13, w2_scale=self.s2,
+                                             logit_bias=lbias, w13_scale=self.s13, w2_scale=self.s2,
                                              ids=ids, weights=wts, ws=ws)
             else:
-                bm.beam_moe_forward(self.cfg, x, self.wr, self.w13, self.w2, logit_bias=self.bias,
+                bm.beam_moe_forward(self.cfg, x, self.wr, self.w13, self.w2, logit_bias=lbias,
                                     w13_scale=self.s13, w2_scale=self.s2, y=y, ids=ids, weights=wts, ws=ws)
 
         for _ in range(warmup):
@@ -252,8 +260,16 @@ def main():
     layer_wbytes = r["n_active"] * 3 * w.I * w.H * wbytes
     extra = {"layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
              "layer_weight_gbs": round(layer_wbytes / (ms_per_step / 1e3) / 1e9, 1),
-             "distinct_experts": r["n_active"], "ms_gpu_events": round(r["ms_gpu"], 4),
-             "ms_wall": round(r["ms_wall"], 4), "kernel_ms": r["kernel_ms"]}
+             "distinct_experts": r["n_active"], "max_rows_per_expert": r["max_rows"],
+             "ms_gpu_events": round(r["ms_gpu"], 4), "ms_wall": round(r["ms_wall"], 4),
+             "kernel_ms": r["kernel_ms"]}
+
+    # ---- the decode batch on the same weights (the HBM-bound half of the metric) ----
+    wd = WORKLOADS["beam_decode_t16"]
+    same_layer = (not w.dense and (w.H, w.I, w.E, w.G, w.Kg, w.K, w.weight_dtype, w.seed) ==
+                  (wd.H, wd.I, wd.E, wd.G, wd.Kg, wd.K, wd.weight_dtype, wd.seed))
+    if not args.no_decode and same_layer and w.name != wd.name:
+        extra["decode_t16"] = decode_line(layer, wd, K, args.warmup)
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
@@ -273,6 +289,36 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_line(layer, wd, steps: int, warmup: int) -> dict:
+    """The decode batch (16 tokens, x RMS-normalised, no logit offsets) through the
+    layer's weights, timed like the main line: step time, gate/up GEMM time and its HBM
+    roofline fraction."""
+    import torch
+    from beam_inputs import token_inputs, to_bf16_bits
+    xd = torch.from_numpy(to_bf16_bits(token_inputs(wd)).view(np.int16)).to(layer.dev).view(torch.bfloat16)
+    log(f"[bench] decode batch T={wd.T} on the same weights ...")
+    r = layer.measure(wd.T, max(steps, 20), warmup, x_rows=xd, bias=None)
+    roof = gate_up_roofline(wd, wd.T, r["n_active"], r["kernel_ms"]["gate_up"])
+    roof["traffic"] = measured_traffic(wd.name)
+    layer_wbytes = r["n_active"] * 3 * wd.I * wd.H * 2
+    return {"workload": wd.name, "T": wd.T, "ms_per_step": round(r["ms_per_step"], 4),
+            "tokens_per_s": round(wd.T / (r["ms_per_step"] / 1e3), 1), "distinct_experts": r["n_active"],
+            "layer_weight_gbs": round(layer_wbytes / (r["ms_per_step"] / 1e3) / 1e9, 1),
+            "layer_hbm_frac": round(layer_wbytes / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": roof, "kernel_ms": r["kernel_ms"]}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measured_traffic(workload: str):
@@ -335,6 +381,7 @@ def cpu_baseline(w, inp, n_tok):
     log(f"[bench] CPU oracle: {runs} runs, {dt:.2f}s each")
     what = "float64 dense SwiGLU MLP" if w.dense else "FP32 routing + float64 expert MLPs and combine"
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(max(oracle.num_threads(), blas)),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "kind": "oracle", "seconds": round(total, 2), "runs": runs,
             "sample": f"first {n} tokens of {w.name}, {runs} runs: {what}"}
 
