@@ -292,6 +292,32 @@ typedef enum {
 
 int beam_moe_time_kernel(int kernel, void* const* events, int n_pairs);
 
+/*
+ * beam_moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The intermediates live in a static device array of
+ * BEAM_MOE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on until
+ * the process ends; its address is looked up once per device, on the first call with
+ * that device current.  The call allocates nothing and frees nothing.
+ *   Arguments and results are those of beam_moe_forward (ids_out / weights_out may be
+ *   NULL as there).
+ *   Returns BEAM_ERR_WORKSPACE, before anything is enqueued, when
+ *   beam_moe_workspace_size(cfg, T) exceeds BEAM_MOE_NOALLOC_SCRATCH_BYTES (Beam's BF16
+ *   layer: up to about 300 tokens), and BEAM_ERR_HIP if the scratch address cannot be
+ *   found on the current device.
+ *   Every call on one device shares that device's array and leaves its contents
+ *   behind; nothing in it has to start at zero (each call writes every region it later
+ *   reads).  Calls that overlap in time on one device -- from several threads or on
+ *   several streams without ordering between them -- race on the array.
+ */
+#define BEAM_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int beam_moe_forward_noalloc(const beam_moe_config* cfg, int64_t T, const void* x,
+                             const float* w_router, const float* logit_bias,
+                             const float* select_bias, const void* w13,
+                             const void* w13_scale, const void* w2, const void* w2_scale,
+                             void* y, int32_t* ids_out, float* weights_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ BEAM_FP8_SCALES_FP32, BEAM_FP8_SCALES_POW2 = range(2)
 C_FUNCTIONS = ("beam_moe_status_string", "beam_moe_abi_version", "beam_moe_workspace_size",
                "beam_moe_workspace_map", "beam_moe_route", "beam_moe_forward",
                "beam_moe_sublayer_forward", "beam_moe_time_kernel", "beam_dense_workspace_size",
-               "beam_dense_forward", "beam_dense_sublayer_forward")
+               "beam_dense_forward", "beam_dense_sublayer_forward", "beam_moe_forward_noalloc")
 BEAM_KERNEL_NONE, BEAM_KERNEL_ROUTER_LOGITS, BEAM_KERNEL_GATE_UP, BEAM_KERNEL_DOWN, BEAM_KERNEL_COMBINE = range(5)
 
 
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.beam_dense_workspace_size.argtypes = [cfgp, i64]
     L.beam_dense_forward.restype = ctypes.c_int
     L.beam_dense_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_forward_noalloc.restype = ctypes.c_int
+    L.beam_moe_forward_noalloc.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.beam_dense_sublayer_forward.restype = ctypes.c_int
     L.beam_dense_sublayer_forward.argtypes = [cfgp, i64, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz,
                                               vp]
@@ -175,6 +177,23 @@ def beam_moe_forward(cfg, x, w_router, w13, w2, logit_bias=None, w13_scale=None,
                                 _ptr(select_bias), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(ids), _ptr(weights),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "beam_moe_forward")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20       # BEAM_MOE_NOALLOC_SCRATCH_BYTES
+
+
+def beam_moe_forward_noalloc(cfg, x, w_router, w13, w2, logit_bias=None, w13_scale=None, w2_scale=None, y=None,
+                             ids=None, weights=None, stream=None, select_bias=None):
+    """beam_moe_forward on the library's static per-device scratch array (no workspace;
+    the library allocates nothing).  y must be given by callers that cannot allocate."""
+    import torch
+    T = x.shape[0]
+    y = torch.empty_like(x) if y is None else y
+    st = lib().beam_moe_forward_noalloc(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                        _ptr(select_bias), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                        _ptr(y), _ptr(ids), _ptr(weights), _stream(stream))
+    _check(st, "beam_moe_forward_noalloc")
     return y
 
 

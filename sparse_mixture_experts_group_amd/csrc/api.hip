@@ -636,6 +636,55 @@ int beam_dense_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h, 
     return launch_status();
 }
 
+}  // extern "C"
+
+// The no-allocation forward's intermediates: one copy of this array per device.  In host
+// code the name stands for a host-side shadow, not a device address: kernels are given
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[BEAM_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BEAM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return BEAM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return BEAM_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_moe_forward_noalloc(const beam_moe_config* cfg, int64_t T, const void* x, const float* w_router,
+                             const float* logit_bias, const float* select_bias, const void* w13,
+                             const void* w13_scale, const void* w2, const void* w2_scale, void* y,
+                             int32_t* ids_out, float* weights_out, void* stream) {
+    int s = check_common(cfg, T);
+    if (s != BEAM_OK) return s;
+    if (T == 0) return BEAM_OK;
+    if (make_layout(*cfg, T).total > BEAM_MOE_NOALLOC_SCRATCH_BYTES) return BEAM_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((s = scratch_address(&ws)) != BEAM_OK) return s;
+    return beam_moe_forward(cfg, T, x, w_router, logit_bias, select_bias, w13, w13_scale, w2, w2_scale, y, ids_out,
+                            weights_out, ws, BEAM_MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int beam_moe_time_kernel(int kernel, void* const* events, int n_pairs) {
     if (kernel < BEAM_KERNEL_NONE || kernel > BEAM_KERNEL_COMBINE || n_pairs < 0) return BEAM_ERR_INVALID_ARG;
     if (n_pairs > 0 && !events) return BEAM_ERR_INVALID_ARG;

@@ -201,3 +201,19 @@ def test_dense_argument_errors_before_any_launch():
     assert sub(bm.make_dense_config(act_dtype=bm.BEAM_DTYPE_F32, weight_dtype=bm.BEAM_DTYPE_F32), 10,
                1 << 40) == bm.BEAM_ERR_UNSUPPORTED
     assert sub(c, 10, 16) == bm.BEAM_ERR_WORKSPACE
+
+
+def test_noalloc_forward_refuses_beyond_the_static_scratch():
+    """The no-allocation forward checks the workspace its call needs against the static
+    scratch size on the host, before it looks up the scratch or enqueues anything."""
+    L = bm.lib()
+    c = beam()
+    assert bm.beam_moe_workspace_size(c, 4096) > bm.NOALLOC_SCRATCH_BYTES
+    call = lambda cfg, T: L.beam_moe_forward_noalloc(ctypes.byref(cfg), T, FAKE, FAKE, None, None, FAKE, None,
+                                                     FAKE, None, FAKE, None, None, None)
+    assert call(c, 4096) == bm.BEAM_ERR_WORKSPACE
+    assert call(c, 0) == bm.BEAM_OK
+    assert call(beam(n_groups=3), 16) == bm.BEAM_ERR_INVALID_ARG
+    assert call(beam(hidden=5000), 16) == bm.BEAM_ERR_UNSUPPORTED
+    # Beam's BF16 decode batch fits
+    assert bm.beam_moe_workspace_size(c, 16) <= bm.NOALLOC_SCRATCH_BYTES
