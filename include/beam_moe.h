@@ -215,10 +215,14 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
  *                in ascending pair order)
  *   hidden       [T*K, I] SwiGLU activations in row order (BF16; FP32 for F32 weights)
  *   expert_out   [T*K, H] expert outputs in row order (BF16; FP32 for F32 weights)
+ *   scores       [T, E] FP32 sigmoid scores s = 1 / (1 + exp(-z)) of the routing contract
+ *   xhat         [T, H] FP32 normalised input RMSNorm(h) * pre_gain (written by the
+ *                sublayer call with BF16 activations)
  * Returns BEAM_OK, or BEAM_ERR_INVALID_ARG for a bad config / T.
  */
 typedef struct beam_moe_ws_map {
     size_t logits, expert_count, expert_off, row_of_pair, pair_of_row, hidden, expert_out;
+    size_t scores, xhat;
     size_t total;
 } beam_moe_ws_map;
 

@@ -36,7 +36,8 @@ class beam_moe_config(ctypes.Structure):
 
 class beam_moe_ws_map(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("logits", "expert_count", "expert_off", "row_of_pair",
-                                               "pair_of_row", "hidden", "expert_out", "total")]
+                                               "pair_of_row", "hidden", "expert_out", "scores", "xhat",
+                                               "total")]
 
 
 class BeamMoEError(RuntimeError):

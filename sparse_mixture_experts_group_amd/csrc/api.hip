@@ -86,7 +86,7 @@ bool config_supported(const beam_moe_config* c) {
 }
 
 struct Layout {
-    size_t z, zpart, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
+    size_t z, scores, zpart, ids, wts, blk_cnt, blk_off, pair_rank, exp_cnt, exp_off, tiles, meta, active;
     size_t row_of_pair, pair_of_row, xhat32, x16, x8, x8s, hbuf, h8, h8s, yperm, part;
     size_t total;
     int nblk, max_tiles, bm;
@@ -127,6 +127,7 @@ Layout make_layout(const beam_moe_config& c, int64_t T, bool dense = false) {
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
     L.z = take(dense ? 0 : sizeof(float) * T * E);
+    L.scores = take(dense ? 0 : sizeof(float) * T * E);
     // chunk sums of the small-T router kernel (only used below the tiled kernel's range)
     L.zpart = take((!dense && router_uses_partials(T, static_cast<int>(H), static_cast<int>(E)))
                        ? sizeof(float) * 64 * T * E : 0);
@@ -219,7 +220,7 @@ void run_router(const beam_moe_config& c, int64_t T, const Layout& L, void* ws, 
                              at<float>(ws, L.zpart));
     }
     launch_router_select(st, static_cast<int>(T), E, c.n_groups, c.topk_groups, K, c.routed_scale, z, select_bias,
-                         ids, wts, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank));
+                         ids, wts, at<int32_t>(ws, L.blk_cnt), at<int32_t>(ws, L.pair_rank), at<float>(ws, L.scores));
     if (!permute) return;
     if (L.nblk <= kFinishSmallBlocks) {
         launch_route_finish_small(st, static_cast<int>(T), K, E, L.nblk, L.bm, ids, at<int32_t>(ws, L.pair_rank),
@@ -400,6 +401,8 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
     out->pair_of_row = L.pair_of_row;
     out->hidden = L.hbuf;
     out->expert_out = L.yperm;
+    out->scores = L.scores;
+    out->xhat = L.xhat32;
     out->total = L.total;
     return BEAM_OK;
 }

@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256) void prenorm_rows(int64_t T, int H, const uint
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) p = __fadd_rn(p, __shfl_xor(p, o, kWave));
     const float ms = __fdiv_rn(__shfl(p, 0, kWave), static_cast<float>(H));
-    const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, eps)));
+    // __builtin_sqrtf is lowered to the correctly rounded sequence (the hardware square
+    // root, then a residual check of its neighbours); __fsqrt_rn is the bare v_sqrt_f32,
+    // which misses by an ulp on some inputs (seen on gfx950 for ms + eps = 1e-6)
+    const float r = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, eps)));
     float am = 0.0f;
     for (int c = lane * 4; c < H; c += 256) {
         float v[4];

@@ -61,6 +61,16 @@ __device__ __forceinline__ int wide_dma_chunk(int lane, int odd) {
 
 constexpr int kUnitScale = 0x7f;                 // E8M0 code of 2^0
 
+// Waves per block.  With 4 the accumulators of a 128 x 128 wave tile fill the AGPRs, and
+// the significand fold of FP8 blocks with general scales (MANT) would need three vector
+// instructions per accumulator (AGPR -> VGPR, multiply, back) and spill; with 8 waves of
+// 64 x 128 the accumulators sit in VGPRs and the fold is one multiply each, which runs
+// beside the MFMAs.  Measured on the Beam layer (one MI355X): FP8 sublayer at 8192 tokens
+// with amax / 448 block scales 9.27 ms (4 waves) against 4.11 ms (8); for BF16 and
+// power-of-two scales the two are within 2-3% (skewed 32768 tokens 20.74 / 20.56 ms,
+// 4096 tokens 4.29 / 4.32, FP8 power-of-two sublayer 3.89 / 3.99), so those keep 4.
+template <bool MANT> constexpr int wide_waves() { return MANT ? 8 : 4; }
+
 __device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
     i32x8 r;
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
@@ -92,10 +102,18 @@ template <> struct StepFrags<true> { i32x8 a[4]; i32x8 b[4]; };
 //
 // SPLIT: as in gemm_prefill.hip, the GEMMs of a single weight set split K into
 // g.k_slices slices (FP32 partial sums) over a flat block order.
-template <int MODE, bool GATHER, bool FP8, bool MANT, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
+// WAVES: 4 waves of 128 x 128 (one per SIMD), or 8 waves of 64 x 128 (two per SIMD, so
+// one wave's MFMAs run while the other waits at a barrier or for its loads).  The WR =
+// WAVES / 2 wave rows take the 32-row MFMA tiles in turn: wave row wm owns tiles wm,
+// wm + WR, ...
+template <int MODE, bool GATHER, bool FP8, bool MANT, bool SPLIT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_wide(GroupedGemmArgs g) {
     static_assert(FP8 || !MANT, "block-scale significands are an FP8 feature");
-    constexpr int BM = kPrefillBM, BN = 256, MI = 4, NI = 4;
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+    constexpr int WR = WAVES / 2;                       // wave rows
+    constexpr int BM = kPrefillBM, BN = 256, MI = 8 / WR, NI = 4;
+    constexpr int NB = BN / WAVES;                      // weight rows each wave moves per stage
+    constexpr int JB = NB / 8;                          // its direct-to-LDS loads per stage
     constexpr int EB = FP8 ? 1 : 2;                     // bytes per element (A and B)
     constexpr int BK = kWideRowBytes / EB;              // K per stage
     constexpr int KS = FP8 ? 2 : 4;                     // MFMA K steps per stage
@@ -129,13 +147,13 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     // MFMA row tiles of this wave that hold rows of the expert (wave-uniform; a prefix of
     // the wave's tiles): the others skip their loads, LDS reads and MFMAs.
     const int ntiles = (rows + 31) / 32;
-    const int mvalid = __builtin_amdgcn_readfirstlane(min(MI, max(0, (ntiles - wm + 1) / 2)));
+    const int mvalid = __builtin_amdgcn_readfirstlane(min(MI, max(0, (ntiles - wm + WR - 1) / WR)));
 
     // Direct-to-LDS assignment, 8 rows x 128 bytes per wave instruction.  A: wave (wm, wn)
-    // moves rows (wm + 2 i) * 32 + 16 wn + 8 h + lane / 8 (h < 2) of each of its live row
+    // moves rows (wm + WR i) * 32 + 16 wn + 8 h + lane / 8 (h < 2) of each of its live row
     // tiles i, the rows the pair (wm, 0), (wm, 1) reads; rows past the expert's end
-    // re-load its last row (never read back).  B: wave w moves rows w * 64 + 8 j + lane / 8
-    // (j < 8; for gate/up waves 0-1 move gate rows, 2-3 up rows).
+    // re-load its last row (never read back).  B: wave w moves rows w * NB + 8 j + lane / 8
+    // (j < JB; for gate/up the first half of the waves move gate rows, the rest up rows).
     // Addresses are block-uniform bases plus 32-bit lane offsets (the launcher checks
     // that the activation rows span less than 4 GB; one expert's weights always do).
     const int dr = lane >> 3;
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int rr = min((wm + 2 * i) * 32 + 16 * wn + 8 * h + dr, rows - 1);
+            const int rr = min((wm + WR * i) * 32 + 16 * wn + 8 * h + dr, rows - 1);
             const int64_t arow = GATHER ? g.pair_of_row[row0 + rr] / g.topk : static_cast<int64_t>(row0 + rr);
             aoff[i][h] = static_cast<uint32_t>(arow * g.lda * EB) + wide_dma_chunk(lane, h);
         }
@@ -155,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     };
     const uint8_t* bbase = static_cast<const uint8_t*>(g.w) + static_cast<int64_t>(e) * nw * krow +
                            static_cast<int64_t>(kbeg) * EB;
-    const uint32_t boff = static_cast<uint32_t>(weight_row(wave * 64 + dr) * krow);
+    const uint32_t boff = static_cast<uint32_t>(weight_row(wave * NB + dr) * krow);
     const uint32_t bch0 = wide_dma_chunk(lane, 0), bch1 = wide_dma_chunk(lane, 1);
     const uint32_t bstep = static_cast<uint32_t>(8 * krow);   // bytes between B rows j and j + 1
     const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(abase, (g.a_rows * g.lda - kbeg) * EB);
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     const int l32 = lane & 31, lh = lane >> 5;
     int arow_l[MI], brow_l[NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) arow_l[i] = (wm + 2 * i) * 32 + l32;
+    for (int i = 0; i < MI; ++i) arow_l[i] = (wm + WR * i) * 32 + l32;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         brow_l[i] = (MODE == kGateUp) ? ((i < 2) ? wn * 64 + i * 32 : BN / 2 + wn * 64 + (i - 2) * 32) + l32
@@ -222,17 +240,17 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                 if (i < MV) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        lds_dma16_buf(rsrc_a, As + ((wm + 2 * i) * 32 + 16 * wn + 8 * h) * kWideRowBytes, aoff[i][h], ks);
+                        lds_dma16_buf(rsrc_a, As + ((wm + WR * i) * 32 + 16 * wn + 8 * h) * kWideRowBytes, aoff[i][h], ks);
                 }
         };
-        // weights of stage kt: loads J0 .. J1 - 1 of the wave's 8
+        // weights of stage kt: loads J0 .. J1 - 1 of the wave's JB
         auto dma_b = [&](int slot, int kt, auto j0_tag, auto j1_tag) {
             constexpr int J0 = decltype(j0_tag)::value, J1 = decltype(j1_tag)::value;
             uint8_t* Bs = smem + (kWideASlots + slot) * kWideOpBytes;
             const int ks = kt * kWideRowBytes;
 #pragma unroll
             for (int j = J0; j < J1; ++j)
-                lds_dma16_buf(rsrc_b, Bs + (wave * 64 + 8 * j) * kWideRowBytes, boff + j * bstep + ((j & 1) ? bch1 : bch0),
+                lds_dma16_buf(rsrc_b, Bs + (wave * NB + 8 * j) * kWideRowBytes, boff + j * bstep + ((j & 1) ? bch1 : bch0),
                               ks);
         };
         auto rd = [&](const uint8_t* T, int row, int c) {
@@ -272,7 +290,8 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                 const int sc_lo = __builtin_amdgcn_readlane(s_lo, kt);
                 const int sc_hi = __builtin_amdgcn_readlane(s_hi, kt);
                 if constexpr (MANT && decltype(first_tag)::value) {
-                    // into the units of this block's significands
+                    // into the units of this block's significands, one tile at a time right
+                    // before its MFMA (so few values are in flight between the register files)
                     const float r_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_lo), kt));
                     const float r_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q_hi), kt));
 #pragma unroll
@@ -283,19 +302,24 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                                 const float r = (MODE == kGateUp && ni >= 2) ? r_hi : r_lo;
 #pragma unroll
                                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] *= r;
+                                const int sb = (MODE == kGateUp && ni >= 2) ? sc_hi : sc_lo;
+                                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, sb, 0, kUnitScale);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        if (mi < MV) {
+#pragma unroll
+                            for (int ni = 0; ni < NI; ++ni) {
+                                const int sb = (MODE == kGateUp && ni >= 2) ? sc_hi : sc_lo;
+                                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, sb, 0, kUnitScale);
                             }
                         }
                 }
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-                    if (mi < MV) {
-#pragma unroll
-                        for (int ni = 0; ni < NI; ++ni) {
-                            const int sb = (MODE == kGateUp && ni >= 2) ? sc_hi : sc_lo;
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, sb, 0, kUnitScale);
-                        }
-                    }
             } else {
                 (void)kt;
                 (void)first_tag;
@@ -317,12 +341,12 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
         // Prologue order: A0 B0 A1 B1; wait for stage 0 (A0, B0).  Issue order in the
         // loop: B(kt + 2) during the first K steps of stage kt, A(kt + 2) in its last.
         using I0 = std::integral_constant<int, 0>;
-        using I8 = std::integral_constant<int, 8>;
+        using IJ = std::integral_constant<int, JB>;
         dma_a(0, 0);
-        dma_b(0, 0, I0{}, I8{});
+        dma_b(0, 0, I0{}, IJ{});
         dma_a(1, min(1, nk - 1));
-        dma_b(1, min(1, nk - 1), I0{}, I8{});
-        wait_lds_dma<2 * MV + 8>();
+        dma_b(1, min(1, nk - 1), I0{}, IJ{});
+        wait_lds_dma<2 * MV + JB>();
         lds_pipeline_barrier();
         load_frags(f0, 0, 0, 0);
         int bslot = 0;                                   // weight slot of stage kt (kt % 3)
@@ -334,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
             // step's fragments, then a share of the weights of stage kt + 2
             static_for<0, KS - 1>([&](auto s_tag) {
                 constexpr int s = decltype(s_tag)::value;
-                constexpr int j0 = (8 * s) / (KS - 1), j1 = (8 * (s + 1)) / (KS - 1);
+                constexpr int j0 = (JB * s) / (KS - 1), j1 = (JB * (s + 1)) / (KS - 1);
                 StepFrags<FP8>& cur = (s & 1) ? f1 : f0;
                 StepFrags<FP8>& nxt = (s & 1) ? f0 : f1;
                 __builtin_amdgcn_sched_barrier(0);
@@ -345,8 +369,8 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             });
             // last K step.  Issue order so far ends ... A(kt+1), B(kt+2): stage kt + 1 has
-            // landed once at most the 8 weight loads of stage kt + 2 are in flight.
-            wait_lds_dma<8>();
+            // landed once at most the JB weight loads of stage kt + 2 are in flight.
+            wait_lds_dma<JB>();
             lds_pipeline_barrier();
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(f1, kt, std::false_type{});
@@ -374,23 +398,24 @@ __global__ __launch_bounds__(256) void gemm_wide(GroupedGemmArgs g) {
     // down: 256-byte row segments per wave, staged through LDS for whole-row stores;
     // gate/up (128-byte segments) and FP32 partial sums: stored from the registers
     if constexpr (SPLIT || MODE == kGateUp) {
-        store_wide_tile<MODE, GATHER, FP8, SPLIT>(g, acc, rows, row0, c0, wm, wn, lane, kz);
+        store_wide_tile<MODE, GATHER, FP8, SPLIT, WR>(g, acc, rows, row0, c0, wm, wn, lane, kz);
     } else {
         __syncthreads();                 // every wave is out of its K loop: the LDS is free
-        store_wide_tile_bf16<MODE, GATHER, FP8>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
+        store_wide_tile_bf16<MODE, GATHER, FP8, WR>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
     }
 }
 
 template <int MODE, bool GATHER, bool FP8, bool MANT, bool SPLIT>
 static void launch_wide_inst(hipStream_t st, const GroupedGemmArgs& g, int blocks, int ks) {
-    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, MANT, SPLIT>), static_cast<int>(kWideLds));
+    constexpr int W = wide_waves<MANT>();
+    lds_opt_in(reinterpret_cast<const void*>(&gemm_wide<MODE, GATHER, FP8, MANT, SPLIT, W>), static_cast<int>(kWideLds));
     const size_t lds = kWideLds;
     if (SPLIT) {
         GroupedGemmArgs gs = g;
         gs.k_slices = ks;
-        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT><<<blocks, 256, lds, st>>>(gs);
+        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT, W><<<blocks, 64 * W, lds, st>>>(gs);
     } else {
-        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT><<<blocks, 256, lds, st>>>(g);
+        gemm_wide<MODE, GATHER, FP8, MANT, SPLIT, W><<<blocks, 64 * W, lds, st>>>(g);
     }
 }
 

@@ -267,10 +267,10 @@ __global__ __launch_bounds__(256) void gemm_wide_mx(GroupedGemmArgs g) {
     // down: 256-byte row segments per wave, staged through LDS for whole-row stores;
     // gate/up (128-byte segments) and FP32 partial sums: stored from the registers
     if constexpr (SPLIT || MODE == kGateUp) {
-        store_wide_tile<MODE, GATHER, true, SPLIT>(g, acc, rows, row0, c0, wm, wn, lane, kz);
+        store_wide_tile<MODE, GATHER, true, SPLIT, 2>(g, acc, rows, row0, c0, wm, wn, lane, kz);
     } else {
         __syncthreads();                 // every wave is out of its K loop: the LDS is free
-        store_wide_tile_bf16<MODE, GATHER, true>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
+        store_wide_tile_bf16<MODE, GATHER, true, 2>(g, acc, rows, row0, c0, wm, wn, wave, lane, smem);
     }
 }
 

@@ -245,7 +245,8 @@ __global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E
                                                      int32_t* __restrict__ ids,
                                                      float* __restrict__ wts,
                                                      int32_t* __restrict__ blk_cnt,
-                                                     int32_t* __restrict__ pair_rank) {
+                                                     int32_t* __restrict__ pair_rank,
+                                                     float* __restrict__ scores) {
     __shared__ int32_t s_ids[kSelectTokens * kMaxTopK];
     __shared__ int32_t s_cnt[kMaxExperts];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -270,6 +271,10 @@ __global__ __launch_bounds__(kSelectTokens * 64) void router_select(int T, int E
             s[v] = (e < E) ? router_sigmoid(z[static_cast<int64_t>(t) * E + e]) : -INFINITY;
             rk[v] = (e < E && sel_bias) ? __fadd_rn(s[v], sel_bias[e]) : s[v];
         }
+        // the scores [T, E] for inspection (the lane's V consecutive experts)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (lane * V + v < E) scores[static_cast<int64_t>(t) * E + lane * V + v] = s[v];
         // group top-2 of the ranking values (multiset: a repeated maximum counts twice)
         float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
@@ -382,6 +387,23 @@ __global__ __launch_bounds__(256) void route_col_scan(int nblk, int E, const int
     if (threadIdx.x == 0) exp_cnt[e] = carry;
 }
 
+// Start of expert e's tiles in the tile list, whose order is: experts by tile count, most
+// first (equal counts: lower expert first), each expert's tiles consecutive.  The heavy
+// experts' tiles start the grid, so the last blocks to run are light ones; and experts
+// with the same count sit together, so when no expert has more than two tiles (a few
+// hundred rows per expert) every two-tile expert starts at an even index: its two tiles
+// fall in one group of row tiles that an XCD runs side by side (the GEMMs' block order),
+// and the second reads each weight panel from that XCD's L2.  s_nt: the tile counts of
+// all experts in LDS (written and synchronised by the caller).
+__device__ __forceinline__ int tile_list_base(int e, int E, int nt, const int* s_nt) {
+    int base = 0;
+    for (int i = 0; i < E; ++i) {
+        const int n = s_nt[i];
+        base += (n > nt || (n == nt && i < e)) ? n : 0;
+    }
+    return base;
+}
+
 // One block of 256 threads; thread e owns expert e (E <= 256): expert offsets, the
 // (expert, row-tile) list of the grouped GEMMs and the list of experts with rows.
 __global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* __restrict__ exp_cnt,
@@ -395,8 +417,11 @@ __global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* 
     if (e < E) exp_off[e] = base;
     if (e == 0) exp_off[E] = total_rows;
     const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
+    __shared__ int s_nt[kMaxExperts];
+    if (e < E) s_nt[e] = nt;
     int total_tiles;
-    const int tbase = block_exclusive_scan(nt, sh, total_tiles);
+    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_nt)
+    const int tbase = tile_list_base(e, E, nt, s_nt);
     for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
@@ -437,8 +462,11 @@ __global__ __launch_bounds__(256) void route_finish_small(int T, int K, int E, i
     if (e < E) { exp_off[e] = base; s_off[e] = base; }
     if (e == 0) exp_off[E] = total_rows;
     const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
+    __shared__ int s_nt[kMaxExperts];
+    if (e < E) s_nt[e] = nt;
     int total_tiles;
-    const int tbase = block_exclusive_scan(nt, sh, total_tiles);
+    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_nt)
+    const int tbase = tile_list_base(e, E, nt, s_nt);
     for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
@@ -517,11 +545,11 @@ void launch_router_logits(hipStream_t st, int T, int H, int E, bool x_bf16, cons
 
 void launch_router_select(hipStream_t st, int T, int E, int G, int Kg, int K, float alpha,
                           const float* z, const float* sel_bias, int32_t* ids, float* wts, int32_t* blk_cnt,
-                          int32_t* pair_rank) {
+                          int32_t* pair_rank, float* scores) {
     const int nblk = (T + kSelectTokens - 1) / kSelectTokens;
     const int V = scores_per_lane(E);
     const int nt = kSelectTokens * 64;
-#define BEAM_SEL(VV) router_select<VV><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, sel_bias, ids, wts, blk_cnt, pair_rank)
+#define BEAM_SEL(VV) router_select<VV><<<nblk, nt, 0, st>>>(T, E, G, Kg, K, alpha, z, sel_bias, ids, wts, blk_cnt, pair_rank, scores)
     if (V == 1) BEAM_SEL(1);
     else if (V == 2) BEAM_SEL(2);
     else BEAM_SEL(4);

@@ -57,10 +57,57 @@ def rel_inf(got, ref):
 
 
 def sample_tokens(T, n=16, seed=1):
+    """Tokens 0, T/2 and T-1 plus n distinct random others."""
     rs = np.random.default_rng(seed)
     base = {0, T - 1, T // 2}
-    extra = rs.choice(T, size=min(T, n), replace=False)
-    return np.array(sorted(base | set(int(t) for t in extra)))[:max(n, 3)]
+    extra = [int(t) for t in rs.permutation(T) if int(t) not in base][:n]
+    return np.array(sorted(base | set(extra)))
+
+
+def tile_list(cnt, off, BM=256):
+    """(first row, last row, 32-row blocks) of every (expert, tile) of the LDS-tiled
+    GEMMs, from the routed counts: an expert with n rows gets ceil(n / 256) tiles of whole
+    32-row blocks, as equal as possible."""
+    out = []
+    for e in np.flatnonzero(cnt):
+        n = int(cnt[e])
+        nt, m = (n + BM - 1) // BM, (n + 31) // 32
+        first = [(j * m // nt) * 32 for j in range(nt)] + [n]
+        for j in range(nt):
+            out.append((int(off[e]) + first[j], int(off[e]) + first[j + 1] - 1, (first[j + 1] - first[j] + 31) // 32))
+    return out
+
+
+def row_tiles_per_wave(nblk, waves):
+    """Counts of live 32-row MFMA tiles per wave row of a block with nblk of them (the K
+    loop instances the waves run): 4 waves take them in turn over 2 wave rows, 8 over 4."""
+    wr, mi = waves // 2, 8 // (waves // 2)
+    return {min(mi, max(0, (nblk - wm + wr - 1) // wr)) for wm in range(wr)}
+
+
+def coverage_rows(w, ws, waves):
+    """Rows that put the first and the last row of every tile under test, and the K-loop
+    instances (live row tiles per wave) those tiles run."""
+    m = bm.beam_moe_workspace_map(cfg_of(w), w.T)
+    cnt = ws_region(ws, m["expert_count"], w.E, np.int32)
+    off = ws_region(ws, m["expert_off"], w.E + 1, np.int32)
+    rows, inst = set(), set()
+    for a, b, nblk in tile_list(cnt, off):
+        rows.update((a, b))
+        inst |= row_tiles_per_wave(nblk, waves)
+    return np.array(sorted(rows)), inst - {0}
+
+
+def check_expert_rows(w, ws, rows, yref_rows, tol):
+    """The down GEMM's output rows (expert outputs in expert-sorted order) against the
+    oracle's expert outputs of the same (token, pick) pairs."""
+    m = bm.beam_moe_workspace_map(cfg_of(w), w.T)
+    P = w.T * w.K
+    yp = ws[m["expert_out"]:m["expert_out"] + P * w.H * 2].view(torch.bfloat16).view(P, w.H)
+    got = yp[torch.from_numpy(rows).cuda().long()].float().cpu().numpy().astype(np.float64)
+    err = rel_inf(got, yref_rows)
+    assert err <= tol, err
+    return err
 
 
 def run_forward(w, dev, x, bias, select_bias=None, declared=None):
@@ -218,12 +265,25 @@ def test_beam_bf16_layer(name, T):
     zg = ws_region(ws, m["logits"], w.T * w.E, np.float32).reshape(w.T, w.E)
     assert np.array_equal(zg, z)
     check_permutation(w, ws, ids)
-    # layer output of every token up to T = 300 (every tile of the grid), else sampled
-    tok = np.arange(w.T) if w.T <= 300 else sample_tokens(w.T)
-    yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
+    # layer output of every token up to 4097 tokens; above, the tokens that put the first
+    # and last row of every (expert, tile) of the tiled GEMMs under test, plus a sample
+    if w.T <= 4097:
+        tok = np.arange(w.T)
+    else:
+        rows, inst = coverage_rows(w, ws, waves=4)
+        assert inst == {1, 2, 3, 4}, inst                # every K-loop instance runs on a checked row
+        por = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["pair_of_row"], w.T * w.K, np.int32)
+        tok = np.union1d(por[rows] // w.K, sample_tokens(w.T))
+    yref, outs = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full),
+                                    return_expert_outputs=True)
     yg = y.float().cpu().numpy()[tok].astype(np.float64)
     err = rel_inf(yg, yref)
-    print(f"[case] {name} T={w.T} rel_inf={err:.3e}", flush=True)
+    # the down GEMM's own output: every expert row of the checked tokens
+    rop = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["row_of_pair"], w.T * w.K, np.int32)
+    prow = rop.reshape(w.T, w.K)[tok].reshape(-1)
+    e_rows = check_expert_rows(w, ws, prow, outs.reshape(-1, w.H), TOL[w.weight_dtype])
+    print(f"[case] {name} T={w.T} tokens={len(tok)} rel_inf={err:.3e} expert rows={len(prow)} "
+          f"rel_inf={e_rows:.3e}", flush=True)
     assert err <= TOL[w.weight_dtype]
 
 
@@ -266,18 +326,32 @@ def test_fp8_sublayer(name):
     moe_out = torch.empty_like(h)
     ids = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
     wts = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    ws = bm.alloc_workspace(cfg, w.T)
     bm.beam_moe_sublayer_forward(cfg, h, w.step_k, dev["w_router"], dev["w13"], dev["w2"],
                                  w13_scale=dev["w13_scale"], w2_scale=dev["w2_scale"], moe_out=moe_out, ids=ids,
-                                 weights=wts)
+                                 weights=wts, ws=ws)
     torch.cuda.synchronize()
     h32 = oracle.bf16_to_f32(x)
-    tok = sample_tokens(w.T)
+    # the tokens that put the first and last row of every (expert, tile) under test, plus
+    # a sample; the general-scale GEMMs run 8 waves (1 or 2 live row tiles each), the
+    # power-of-two ones 4
+    waves = 4 if w.fp8_scales == "pow2" else 8
+    rows, inst = coverage_rows(w, ws, waves)
+    assert inst and (waves == 4 or inst == {1, 2}), inst
+    por = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["pair_of_row"], w.T * w.K, np.int32)
+    tok = np.union1d(por[rows] // w.K, sample_tokens(w.T))
     ref = oracle.sublayer_forward(h32, None, None, w.step_k, w.norm_eps, full.w_router, bias, bank_of(w, full),
                                   w.G, w.Kg, w.K, w.alpha, token_subset=tok)
     check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    # expert rows of the checked tokens against the oracle's expert outputs of x-hat
+    _, outs = oracle.moe_combine(ref["xhat"][tok].astype(np.float64), ref["ids"][tok], ref["w"][tok],
+                                 bank_of(w, full), return_expert_outputs=True)
+    rop = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["row_of_pair"], w.T * w.K, np.int32)
+    e_rows = check_expert_rows(w, ws, rop.reshape(w.T, w.K)[tok].reshape(-1), outs.reshape(-1, w.H), TOL[DT_FP8])
     e_moe = rel_inf(moe_out.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
     e_h = rel_inf(h.float().cpu().numpy()[tok].astype(np.float64), ref["h_new"])
-    print(f"[case] sublayer fp8 {w.fp8_scales} moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e}", flush=True)
+    print(f"[case] sublayer fp8 {w.fp8_scales} tokens={len(tok)} moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e} "
+          f"expert rows rel_inf={e_rows:.3e}", flush=True)
     assert e_moe <= TOL[DT_FP8]
     assert e_h <= TOL[DT_FP8]
 
