@@ -324,8 +324,8 @@ def cpu_model() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     passes (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
-    known size), or None when there is no record for this workload or the kernel source
-    has changed since the counters were taken."""
+    known size), or None when there is no record for this workload or a source of the
+    kernel has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -333,9 +333,12 @@ def measured_traffic(workload: str):
     rec = json.load(open(path)).get(workload)
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
-        return None
+    srcs = rec.get("sources", [rec.get("source")])
+    shas = rec.get("sources_sha256", [rec.get("source_sha256")])
+    for name, sha in zip(srcs, shas):
+        src = os.path.join(ROOT, name)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+            return None
     return rec["traffic_bytes_per_launch"]
 
 
