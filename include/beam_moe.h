@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BEAM_MOE_ABI_VERSION 4
+#define BEAM_MOE_ABI_VERSION 5
 
 typedef enum {
     BEAM_OK = 0,
@@ -218,11 +218,18 @@ int beam_moe_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
  *   scores       [T, E] FP32 sigmoid scores s = 1 / (1 + exp(-z)) of the routing contract
  *   xhat         [T, H] FP32 normalised input RMSNorm(h) * pre_gain (written by the
  *                sublayer call with BF16 activations)
+ *   x_q, x_q_scale  FP8 and MXFP4 weights: [T, H] E4M3 codes of the expert input (x, or
+ *                xhat in the sublayer call) and [T] FP32 row scales s = amax / 448 (1 for
+ *                a zero row): code = E4M3(v * (1/s)), 1/s and the product rounded to FP32
+ *   h_q, h_q_scale  the same for the BF16 `hidden` rows: [T*K, I] codes, [T*K] scales
+ *                (the dense MLP's calls keep theirs in their own workspace layout)
+ *                Other weight types: empty regions.
  * Returns BEAM_OK, or BEAM_ERR_INVALID_ARG for a bad config / T.
  */
 typedef struct beam_moe_ws_map {
     size_t logits, expert_count, expert_off, row_of_pair, pair_of_row, hidden, expert_out;
     size_t scores, xhat;
+    size_t x_q, x_q_scale, h_q, h_q_scale;
     size_t total;
 } beam_moe_ws_map;
 

@@ -120,6 +120,53 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return E4M3_TABLE[np.asarray(codes, np.uint8)]
 
 
+def e4m3_encode(v32: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3FN code of each FP32 value, ties to the even code (the one whose
+    mantissa field is even), magnitudes at or past 448 saturated to 448; the sign bit is
+    the value's (so -0 -> 0x80).  Written as a search over the 127 non-negative finite
+    code values (ascending in code order) to stay obviously correct."""
+    v = np.asarray(v32, np.float32)
+    a = np.abs(v.astype(np.float64))
+    pos = E4M3_TABLE[:0x7F]
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 1, 0x7E)
+    lo = hi - 1
+    d_lo, d_hi = a - pos[lo], pos[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= 448.0, 0x7E, code)
+    code = np.where(a == 0.0, 0, code).astype(np.uint8)
+    return code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+
+
+def bf16_round(v32: np.ndarray) -> np.ndarray:
+    """FP32 -> bfloat16 by round to nearest even, returned widened to FP32 (finite
+    inputs)."""
+    b = np.asarray(v32, np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return bf16_to_f32(r.astype(np.uint16))
+
+
+def quant_rows_e4m3(v32: np.ndarray):
+    """E4M3 activation operand of the 8-bit expert GEMMs, one FP32 scale per row: s =
+    amax(|row|) / 448 (1 for an all-zero row), codes = E4M3(v * (1/s)) with 1/s and the
+    product rounded to FP32 -- the FP32 steps, in this order, decide the codes, so they
+    are spelled out.  Returns (codes [R, C] uint8, s [R] float32).  The pages name FP8
+    checkpoints (Reflection Beam 1.0 overview, "Key specifications at a glance") but not
+    the activations' format; E4M3 rows with an amax scale is the plainest reading."""
+    v = np.ascontiguousarray(v32, np.float32)
+    amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    return e4m3_encode((v * inv[:, None]).astype(np.float32)), s
+
+
+def act_e4m3(v32: np.ndarray) -> np.ndarray:
+    """Value the 8-bit GEMMs see for FP32 activation rows: code value * row scale
+    (float64, exact)."""
+    codes, s = quant_rows_e4m3(v32)
+    return e4m3_to_f64(codes) * s.astype(np.float64)[:, None]
+
+
 def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
     """Stored value of a block-scaled E4M3 matrix: code value * its tile's FP32 scale
     (exact in float64)."""
@@ -237,22 +284,41 @@ def silu(g: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g))
 
 
-def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """SwiGLU expert on rows [n,H] (float64): a = SiLU(x Wg^T) * (x Wu^T), o = a Wd^T.
-    w13 [2I,H]: gate rows 0..I-1, up rows I..2I-1; w2 [H,I]."""
+def expert_gate_up(xrows: np.ndarray, w13: np.ndarray, act_quant: bool = False) -> np.ndarray:
+    """SwiGLU hidden rows a = SiLU(x Wg^T) * (x Wu^T) (float64); w13 [2I,H]: gate rows
+    0..I-1, up rows I..2I-1.  act_quant: x (FP32 values) enters as E4M3 rows
+    (`quant_rows_e4m3`), as the 8-bit GEMMs take it."""
     I = w13.shape[0] // 2
+    if act_quant:
+        xrows = act_e4m3(np.asarray(xrows).astype(np.float32))
     g = xrows @ w13[:I].T
     u = xrows @ w13[I:].T
-    a = silu(g) * u
+    return silu(g) * u
+
+
+def expert_down(a: np.ndarray, w2: np.ndarray, act_quant: bool = False) -> np.ndarray:
+    """Expert output o = a Wd^T (float64); w2 [H,I].  act_quant: a is rounded to FP32,
+    stored as BF16 and enters as E4M3 rows, as the 8-bit down GEMM takes it."""
+    if act_quant:
+        a = act_e4m3(bf16_round(np.asarray(a).astype(np.float32)))
     return a @ w2.T
+
+
+def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray, act_quant: bool = False) -> np.ndarray:
+    """SwiGLU expert on rows [n,H] (float64): o = (SiLU(x Wg^T) * (x Wu^T)) Wd^T; with
+    act_quant both GEMMs see the E4M3 operands the library forms; products and sums stay
+    float64."""
+    return expert_down(expert_gate_up(xrows, w13, act_quant), w2, act_quant)
 
 
 class ExpertBank:
     """Float64 view of stored expert weights, decoded one expert at a time."""
 
-    def __init__(self, w13, w2, dtype: str, w13_scale=None, w2_scale=None, block: int = 128):
+    def __init__(self, w13, w2, dtype: str, w13_scale=None, w2_scale=None, block: int = 128,
+                 act_quant: bool = False):
         self.w13, self.w2, self.dtype = w13, w2, dtype
         self.s13, self.s2, self.block = w13_scale, w2_scale, block
+        self.act_quant = act_quant          # E4M3 activation operands (expert_ffn)
 
     def expert(self, e: int):
         if self.dtype == "f32":
@@ -282,12 +348,18 @@ def moe_combine(x64: np.ndarray, ids: np.ndarray, w: np.ndarray, bank: ExpertBan
     for e in np.unique(ids):
         t_idx, k_idx = np.nonzero(ids == e)
         w13, w2 = bank.expert(int(e))
-        outs[t_idx, k_idx] = expert_ffn(x64[t_idx], w13, w2)
-    y = np.zeros((T, H), np.float64)
-    for i in range(K):
-        y += w[:, i:i + 1].astype(np.float64) * outs[:, i]
+        outs[t_idx, k_idx] = expert_ffn(x64[t_idx], w13, w2, bank.act_quant)
+    y = combine_outputs(outs, w)
     if return_expert_outputs:
         return y, outs
+    return y
+
+
+def combine_outputs(outs: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y[t] = sum_i w[t,i] * outs[t,i] (float64), the sum taken in ascending i."""
+    y = np.zeros((outs.shape[0], outs.shape[2]), np.float64)
+    for i in range(outs.shape[1]):
+        y += w[:, i:i + 1].astype(np.float64) * outs[:, i]
     return y
 
 
@@ -308,6 +380,12 @@ def residual_coeffs(k: int):
 def residual_update(h64: np.ndarray, out64: np.ndarray, k: int) -> np.ndarray:
     c1, c2 = residual_coeffs(k)
     return c1 * h64 + c2 * out64
+
+
+def sublayer_output(h32_rows: np.ndarray, y: np.ndarray, post_gain, step_k: int, eps: float) -> np.ndarray:
+    """The stream after a sublayer whose output (before the post-norm) is y: the
+    post-RMSNorm of y, added with the constant-scale residual weights at step k."""
+    return residual_update(h32_rows.astype(np.float64), rmsnorm64(y, post_gain, eps), step_k)
 
 
 # ---------------------------------------------------------------------------
@@ -333,8 +411,7 @@ def sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, eps: flo
     xhat, _ = prenorm(h32, pre_gain, eps)
     r = moe_forward(xhat, w_router, bias, bank, G, Kg, K, alpha, token_subset, select_bias)
     tok = r["tokens"]
-    yn = rmsnorm64(r["y"], post_gain, eps)
-    r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)
+    r["h_new"] = sublayer_output(h32[tok], r["y"], post_gain, step_k, eps)
     r["xhat"] = xhat
     return r
 
@@ -351,7 +428,7 @@ def dense_forward(x32: np.ndarray, bank: ExpertBank, token_subset: np.ndarray | 
     Returns dict(y [n,H] float64, tokens)."""
     tok = np.arange(x32.shape[0]) if token_subset is None else np.asarray(token_subset)
     w13, w2 = bank.expert(0)
-    y = expert_ffn(x32[tok].astype(np.float64), w13, w2)
+    y = expert_ffn(x32[tok].astype(np.float64), w13, w2, bank.act_quant)
     return {"y": y, "tokens": tok}
 
 
@@ -364,7 +441,6 @@ def dense_sublayer_forward(h32: np.ndarray, pre_gain, post_gain, step_k: int, ep
     xhat, _ = prenorm(h32, pre_gain, eps)
     r = dense_forward(xhat, bank, token_subset)
     tok = r["tokens"]
-    yn = rmsnorm64(r["y"], post_gain, eps)
-    r["h_new"] = residual_update(h32[tok].astype(np.float64), yn, step_k)
+    r["h_new"] = sublayer_output(h32[tok], r["y"], post_gain, step_k, eps)
     r["xhat"] = xhat
     return r

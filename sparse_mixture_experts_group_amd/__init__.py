@@ -34,10 +34,13 @@ class beam_moe_config(ctypes.Structure):
                 ("norm_eps", ctypes.c_float), ("fp8_scale_kind", ctypes.c_int32)]
 
 
+ABI_VERSION = 5          # BEAM_MOE_ABI_VERSION of the structures below
+
+
 class beam_moe_ws_map(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("logits", "expert_count", "expert_off", "row_of_pair",
                                                "pair_of_row", "hidden", "expert_out", "scores", "xhat",
-                                               "total")]
+                                               "x_q", "x_q_scale", "h_q", "h_q_scale", "total")]
 
 
 class BeamMoEError(RuntimeError):
@@ -68,6 +71,10 @@ def lib() -> ctypes.CDLL:
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m sparse_mixture_experts_group_amd.build` (no fallback path exists)")
     L = ctypes.CDLL(LIB_PATH)
+    L.beam_moe_abi_version.restype = ctypes.c_int
+    if L.beam_moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI {L.beam_moe_abi_version()}, this binding expects {ABI_VERSION}: "
+                          "rebuild it with `python -m sparse_mixture_experts_group_amd.build`")
     vp, cfgp = ctypes.c_void_p, ctypes.POINTER(beam_moe_config)
     i64, sz = ctypes.c_int64, ctypes.c_size_t
     L.beam_moe_status_string.restype = ctypes.c_char_p

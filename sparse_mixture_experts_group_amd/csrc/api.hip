@@ -403,6 +403,10 @@ int beam_moe_workspace_map(const beam_moe_config* cfg, int64_t T, beam_moe_ws_ma
     out->expert_out = L.yperm;
     out->scores = L.scores;
     out->xhat = L.xhat32;
+    out->x_q = L.x8;
+    out->x_q_scale = L.x8s;
+    out->h_q = L.h8;
+    out->h_q_scale = L.h8s;
     out->total = L.total;
     return BEAM_OK;
 }

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = bm.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert bm.abi_version() == 4
+    assert bm.abi_version() == 5
 
 
 def test_status_strings():
@@ -52,6 +52,11 @@ def test_workspace_size_and_map():
     assert n4k - m["expert_out"] >= 4096 * 8 * 5120 * 2
     assert bm.beam_moe_workspace_size(c, -1) == 0
     assert bm.beam_moe_workspace_size(beam(n_groups=3), 16) == 0
+    # E4M3 activation regions: present for 8-bit weights, empty for BF16
+    assert m["x_q_scale"] == m["x_q"] and m["h_q_scale"] == m["h_q"]
+    f = bm.beam_moe_workspace_map(beam(weight_dtype=bm.BEAM_DTYPE_FP8_E4M3), 4096)
+    assert f["x_q_scale"] - f["x_q"] >= 4096 * 5120 and f["h_q_scale"] - f["h_q"] >= 4096 * 8 * 2560
+    assert all(f[k] % 256 == 0 and f[k] < f["total"] for k in ("x_q", "x_q_scale", "h_q", "h_q_scale"))
 
 
 @pytest.mark.parametrize("kw", [dict(n_groups=3), dict(n_groups=256), dict(topk_groups=9), dict(topk=0),

@@ -17,6 +17,10 @@ pytestmark = pytest.mark.gpu
 # MXFP4 weights are exact as stored on both sides; the GPU error is the E4M3 activation
 # quantisation, as on the FP8 path
 TOL = {DT_F32: 1e-5, DT_BF16: 2e-2, DT_FP8: 6e-2, DT_MXFP4: 6e-2}
+# 8-bit weights against the oracle with the same E4M3 activation operands
+# (ExpertBank(act_quant=True)): what remains is FP32 accumulation and BF16 storage of h
+# and of the expert outputs, as on the BF16 path
+TOL_Q = 2e-2
 
 
 def scale_kind(w, declared=None):
@@ -43,9 +47,72 @@ def x_f32(w, x):
     return x if w.act_dtype == DT_F32 else oracle.bf16_to_f32(x)
 
 
-def bank_of(w, full):
+def bank_of(w, full, act_quant=False):
     return oracle.ExpertBank(full.w13, full.w2, DTYPE_NAMES[w.weight_dtype], full.w13_scale, full.w2_scale,
-                             w.fp8_block)
+                             w.fp8_block, act_quant=act_quant)
+
+
+def zero_sign(codes):
+    """E4M3 codes with -0 (0x80) read as +0: both are the value 0."""
+    return np.where((codes & 0x7F) == 0, 0, codes).astype(np.uint8)
+
+
+def check_act_codes(ws, off_q, off_s, rows_sel, v32):
+    """E4M3 activation codes and row scales the GPU wrote (rows `rows_sel` of the region)
+    against the oracle's quantisation of the same FP32 values, bit for bit."""
+    n = v32.shape[1]
+    R = int(rows_sel.max()) + 1 if len(rows_sel) else 0
+    q = ws[off_q:off_q + R * n].view(R, n)[torch.from_numpy(rows_sel).cuda().long()].cpu().numpy()
+    sc = ws[off_s:off_s + 4 * R].view(torch.float32)[torch.from_numpy(rows_sel).cuda().long()].cpu().numpy()
+    ref_q, ref_s = oracle.quant_rows_e4m3(v32)
+    assert np.array_equal(sc.view(np.uint32), ref_s.view(np.uint32)), "row scales differ"
+    bad = int((zero_sign(q) != zero_sign(ref_q)).sum())
+    assert bad == 0, f"{bad} E4M3 codes differ"
+
+
+def expert_refs(bank, x64, ids, h_rows=None):
+    """One pass over the routed experts of the checked tokens (each decoded once):
+    outs    plain expert outputs (float64 operands);
+    outs_q  outputs with the E4M3 operands the library forms (oracle act_quant);
+    a_q     the gate/up GEMM's SwiGLU rows from E4M3 x, before BF16 storage;
+    down_x  given the GPU's own BF16 SwiGLU rows of the pairs (h_rows [n, K, I] FP32):
+            the down GEMM's result on exactly those operands."""
+    n, K = ids.shape
+    H = x64.shape[1]
+    outs = np.zeros((n, K, H))
+    outs_q = np.zeros((n, K, H))
+    down_x = np.zeros((n, K, H)) if h_rows is not None else None
+    a_q = None
+    for e in np.unique(ids):
+        t_idx, k_idx = np.nonzero(ids == e)
+        w13, w2 = bank.expert(int(e))
+        xs = x64[t_idx]
+        outs[t_idx, k_idx] = oracle.expert_ffn(xs, w13, w2)
+        a = oracle.expert_gate_up(xs, w13, act_quant=True)
+        if a_q is None:
+            a_q = np.zeros((n, K, a.shape[1]))
+        a_q[t_idx, k_idx] = a
+        outs_q[t_idx, k_idx] = oracle.expert_down(a, w2, act_quant=True)
+        if h_rows is not None:
+            down_x[t_idx, k_idx] = oracle.expert_down(h_rows[t_idx, k_idx], w2, act_quant=True)
+    return outs, outs_q, a_q, down_x
+
+
+def gpu_rows(ws, off, P, width, rows):
+    """BF16 rows `rows` of a [P, width] workspace region, widened to FP32."""
+    r = ws[off:off + P * width * 2].view(P, width * 2)[torch.from_numpy(np.asarray(rows)).cuda().long()]
+    return oracle.bf16_to_f32(r.cpu().numpy().view(np.uint16))
+
+
+def check_gpu_act_codes(w, cfg, ws, x32_rows, tok, rows):
+    """x (or x-hat) codes of tokens `tok` from their FP32 values, and the codes of the
+    GPU's own BF16 SwiGLU rows `rows`."""
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    check_act_codes(ws, m["x_q"], m["x_q_scale"], np.asarray(tok), x32_rows)
+    P = w.T * w.K
+    hid = ws[m["hidden"]:m["hidden"] + P * w.I * 2].view(P, w.I * 2)[torch.from_numpy(rows).cuda().long()]
+    h32 = oracle.bf16_to_f32(hid.cpu().numpy().view(np.uint16))
+    check_act_codes(ws, m["h_q"], m["h_q_scale"], np.asarray(rows), h32)
 
 
 def dev_bias(bias):
@@ -108,6 +175,15 @@ def check_expert_rows(w, ws, rows, yref_rows, tol):
     err = rel_inf(got, yref_rows)
     assert err <= tol, err
     return err
+
+
+def layer_errors(w, cfg, ws, y, x32, tok, rid, rw, bank):
+    """Layer output of tokens `tok` against the oracle with plain and with E4M3
+    operands, one pass over the experts."""
+    outs, outs_q, _, _ = expert_refs(bank, x32[tok].astype(np.float64), rid[tok])
+    got = y.float().cpu().numpy()[tok].astype(np.float64)
+    return (rel_inf(got, oracle.combine_outputs(outs, rw[tok])),
+            rel_inf(got, oracle.combine_outputs(outs_q, rw[tok])))
 
 
 def run_forward(w, dev, x, bias, select_bias=None, declared=None):
@@ -338,22 +414,40 @@ def test_fp8_sublayer(name):
     waves = 4 if w.fp8_scales == "pow2" else 8
     rows, inst = coverage_rows(w, ws, waves)
     assert inst and (waves == 4 or inst == {1, 2}), inst
-    por = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["pair_of_row"], w.T * w.K, np.int32)
+    m = bm.beam_moe_workspace_map(cfg, w.T)
+    P = w.T * w.K
+    por = ws_region(ws, m["pair_of_row"], P, np.int32)
+    rop = ws_region(ws, m["row_of_pair"], P, np.int32)
     tok = np.union1d(por[rows] // w.K, sample_tokens(w.T))
-    ref = oracle.sublayer_forward(h32, None, None, w.step_k, w.norm_eps, full.w_router, bias, bank_of(w, full),
-                                  w.G, w.Kg, w.K, w.alpha, token_subset=tok)
-    check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
-    # expert rows of the checked tokens against the oracle's expert outputs of x-hat
-    _, outs = oracle.moe_combine(ref["xhat"][tok].astype(np.float64), ref["ids"][tok], ref["w"][tok],
-                                 bank_of(w, full), return_expert_outputs=True)
-    rop = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["row_of_pair"], w.T * w.K, np.int32)
-    e_rows = check_expert_rows(w, ws, rop.reshape(w.T, w.K)[tok].reshape(-1), outs.reshape(-1, w.H), TOL[DT_FP8])
-    e_moe = rel_inf(moe_out.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
-    e_h = rel_inf(h.float().cpu().numpy()[tok].astype(np.float64), ref["h_new"])
-    print(f"[case] sublayer fp8 {w.fp8_scales} tokens={len(tok)} moe rel_inf={e_moe:.3e} h rel_inf={e_h:.3e} "
-          f"expert rows rel_inf={e_rows:.3e}", flush=True)
-    assert e_moe <= TOL[DT_FP8]
-    assert e_h <= TOL[DT_FP8]
+    # routing of every token
+    xhat, _ = oracle.prenorm(h32, None, w.norm_eps)
+    rid, rw = oracle.route(oracle.router_logits(xhat, full.w_router, bias), w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+    # the E4M3 operands bit for bit: x-hat codes of every token, SwiGLU codes of the rows
+    # of the checked tokens
+    trows = rop.reshape(w.T, w.K)[tok].reshape(-1)
+    check_gpu_act_codes(w, cfg, ws, xhat, np.arange(w.T), trows)
+    # each GEMM on its exact operands, and the layer against the oracle with and without
+    # the E4M3 operands
+    hid = gpu_rows(ws, m["hidden"], P, w.I, trows).reshape(len(tok), w.K, w.I)
+    outs, outs_q, a_q, down_x = expert_refs(bank_of(w, full), xhat[tok].astype(np.float64), rid[tok], hid)
+    e_gu = rel_inf(hid.astype(np.float64), a_q)
+    e_dn = check_expert_rows(w, ws, trows, down_x.reshape(-1, w.H), TOL_Q)
+    e_rows = check_expert_rows(w, ws, trows, outs.reshape(-1, w.H), TOL[DT_FP8])
+    y_got = moe_out.float().cpu().numpy()[tok].astype(np.float64)
+    h_got = h.float().cpu().numpy()[tok].astype(np.float64)
+    res = {}
+    for name, o in (("plain", outs), ("E4M3 operands", outs_q)):
+        y_ref = oracle.combine_outputs(o, rw[tok])
+        res[name] = (rel_inf(y_got, y_ref), rel_inf(h_got, oracle.sublayer_output(h32[tok], y_ref, None, w.step_k,
+                                                                                  w.norm_eps)))
+    print(f"[case] sublayer fp8 {w.fp8_scales} tokens={len(tok)} gate/up rows rel_inf={e_gu:.3e} "
+          f"down rows rel_inf={e_dn:.3e} (plain oracle {e_rows:.3e}); moe, h rel_inf: plain "
+          f"{res['plain'][0]:.3e}, {res['plain'][1]:.3e}; E4M3 operands {res['E4M3 operands'][0]:.3e}, "
+          f"{res['E4M3 operands'][1]:.3e}", flush=True)
+    assert e_gu <= TOL_Q
+    assert max(res["plain"]) <= TOL[DT_FP8]
+    assert max(res["E4M3 operands"]) <= TOL_Q
 
 
 @pytest.mark.parametrize("scales,declared", [("amax", None), ("pow2", None),
@@ -377,10 +471,11 @@ def test_fp8_forward(T, scales, declared):
     check_routing(w, ids, wts, rid, rw)
     check_permutation(w, ws, ids)
     tok = np.arange(T) if T <= 300 else sample_tokens(T)
-    yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
-    err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
-    print(f"[case] fp8 forward {scales} T={T} rel_inf={err:.3e}", flush=True)
+    check_gpu_act_codes(w, cfg, ws, x32, np.arange(T), np.arange(T * w.K))
+    err, err_q = layer_errors(w, cfg, ws, y, x32, tok, rid, rw, bank_of(w, full))
+    print(f"[case] fp8 forward {scales} T={T} rel_inf={err:.3e} (E4M3 operands modelled: {err_q:.3e})", flush=True)
     assert err <= TOL[DT_FP8]
+    assert err_q <= TOL_Q
 
 
 # ---------------------------------------------------------------------------
@@ -402,10 +497,12 @@ def test_mxfp4_forward(name, T):
     check_routing(w, ids, wts, rid, rw)
     check_permutation(w, ws, ids)
     tok = np.arange(T) if T <= 300 else sample_tokens(T)
-    yref = oracle.moe_combine(x32[tok].astype(np.float64), rid[tok], rw[tok], bank_of(w, full))
-    err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), yref)
-    print(f"[case] mxfp4 forward T={T} rel_inf={err:.3e}", flush=True)
+    rop = ws_region(ws, bm.beam_moe_workspace_map(cfg, T)["row_of_pair"], T * w.K, np.int32)
+    check_gpu_act_codes(w, cfg, ws, x32, np.arange(T), rop.reshape(T, w.K)[tok].reshape(-1))
+    err, err_q = layer_errors(w, cfg, ws, y, x32, tok, rid, rw, bank_of(w, full))
+    print(f"[case] mxfp4 forward T={T} rel_inf={err:.3e} (E4M3 operands modelled: {err_q:.3e})", flush=True)
     assert err <= TOL[DT_MXFP4]
+    assert err_q <= TOL_Q
 
 
 
@@ -415,13 +512,14 @@ def test_mxfp4_forward(name, T):
 _DENSE_BANK = {}
 
 
-def dense_bank(w, full):
+def dense_bank(w, full, act_quant=False):
     """Float64 weights of the dense MLP, decoded once per weight dtype."""
     key = (w.weight_dtype, w.fp8_scales)
     if key not in _DENSE_BANK:
         w13, w2 = bank_of(w, full).expert(0)
-        _DENSE_BANK[key] = oracle.ExpertBank(w13[None], w2[None], "f32")
-    return _DENSE_BANK[key]
+        _DENSE_BANK[key] = (w13[None], w2[None])
+    w13, w2 = _DENSE_BANK[key]
+    return oracle.ExpertBank(w13, w2, "f32", act_quant=act_quant)
 
 
 def dense_cfg(w):
@@ -451,9 +549,15 @@ def test_dense_forward(dt, T):
     ref = oracle.dense_forward(x_f32(w, x), dense_bank(w, full), token_subset=tok)
     got = y.float().cpu().numpy()[tok].astype(np.float64)
     err = rel_inf(got, ref["y"])
-    print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T} rel_inf={err:.3e}", flush=True)
+    msg = ""
+    if dt in (DT_FP8, DT_MXFP4):
+        err_q = rel_inf(got, oracle.dense_forward(x_f32(w, x), dense_bank(w, full, True), token_subset=tok)["y"])
+        msg = f" (E4M3 operands modelled: {err_q:.3e})"
+    print(f"[case] dense forward {DTYPE_NAMES[dt]} T={T} rel_inf={err:.3e}{msg}", flush=True)
     assert np.isfinite(got).all()
     assert err <= TOL[dt]
+    if msg:
+        assert err_q <= TOL_Q
 
 
 @pytest.mark.parametrize("dt,T", [(DT_BF16, 300), (DT_FP8, 16)])
@@ -476,6 +580,13 @@ def test_dense_sublayer(dt, T):
     e_h = rel_inf(h.float().cpu().numpy().astype(np.float64), ref["h_new"])
     print(f"[case] dense sublayer {DTYPE_NAMES[dt]} T={T} mlp rel_inf={e_y:.3e} h rel_inf={e_h:.3e}", flush=True)
     assert e_y <= TOL[dt] and e_h <= TOL[dt]
+    if dt == DT_FP8:
+        refq = oracle.dense_sublayer_forward(oracle.bf16_to_f32(x), g1, g2, w.step_k, w.norm_eps,
+                                             dense_bank(w, full, True))
+        q_y = rel_inf(out.float().cpu().numpy().astype(np.float64), refq["y"])
+        q_h = rel_inf(h.float().cpu().numpy().astype(np.float64), refq["h_new"])
+        print(f"[case] dense sublayer E4M3 operands modelled: mlp rel_inf={q_y:.3e} h rel_inf={q_h:.3e}", flush=True)
+        assert q_y <= TOL_Q and q_h <= TOL_Q
 
 
 # ---------------------------------------------------------------------------
@@ -546,3 +657,7 @@ def test_config_limits_and_degenerate_routing(case, T):
     err = rel_inf(y.float().cpu().numpy()[tok].astype(np.float64), ref["y"])
     print(f"[case] edge {case} T={T} rel_inf={err:.3e}", flush=True)
     assert err <= TOL[w.weight_dtype]
+    if w.weight_dtype in (DT_FP8, DT_MXFP4):
+        _, err_q = layer_errors(w, cfg, ws, y, x_f32(w, full.x), tok, ref["ids"], ref["w"], bank_of(w, full))
+        print(f"[case] edge {case} E4M3 operands modelled: rel_inf={err_q:.3e}", flush=True)
+        assert err_q <= TOL_Q

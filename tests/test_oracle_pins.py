@@ -509,6 +509,89 @@ def test_mxfp4_dequant_layout_and_blocks():
     assert np.array_equal(v, exp)
 
 
+def test_e4m3_encode_matches_torch_and_spec():
+    """The oracle's E4M3 rounding (activation operands) against torch's float8_e4m3fn
+    conversion (round to nearest even) on values from the subnormal range to 448, on every
+    midpoint between neighbouring codes (the ties) and on every code value; magnitudes
+    past 448 saturate to 448 (torch returns NaN from 464 on)."""
+    import torch
+    rs = np.random.default_rng(5)
+    v = (rs.standard_normal(400_000) * np.exp(rs.uniform(-14, 6, 400_000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    pos = oracle.E4M3_TABLE[:0x7F]
+    mid = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([v, mid, -mid, pos.astype(np.float32), -pos.astype(np.float32)])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(v), ref)
+    # ties go to the even code: 1 + 1/16 (between 1 and 1.125) -> 1.0, 1 + 3/16 -> 1.25
+    assert oracle.e4m3_encode(np.float32([1.0625, 1.1875])).tolist() == [0x38, 0x3A]
+    assert oracle.e4m3_encode(np.float32([460.0, 500.0, -1e9, 0.0, -0.0])).tolist() == [0x7E, 0x7E, 0xFE, 0x00, 0x80]
+
+
+def test_bf16_round_matches_torch_including_ties():
+    import torch
+    rs = np.random.default_rng(6)
+    b = rs.integers(0, 2 ** 32, 300_000, dtype=np.uint64).astype(np.uint32)
+    b = b[np.isfinite(b.view(np.float32))]
+    ties = (b & np.uint32(0xFFFF0000)) | np.uint32(0x8000)        # exactly half way
+    v = np.concatenate([b, ties[np.isfinite(ties.view(np.float32))]]).view(np.float32)
+    v = v[np.abs(v) < 3e38]
+    ref = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.bf16_round(v).view(np.uint32), ref.view(np.uint32))
+
+
+def test_quant_rows_e4m3_closed_forms():
+    """Row E4M3 quantisation: a row whose amax is 448 * 2^k has the scale 2^k exactly and
+    its E4M3-representable multiples come back unchanged; an all-zero row gets scale 1
+    and zero codes; the amax element becomes +-448; negating a row flips only sign bits;
+    every value is within half an E4M3 step of its input (relative 2^-4 in the normal
+    range, 2^-10 s below it)."""
+    rs = np.random.default_rng(7)
+    grid = oracle.E4M3_TABLE[:0x7F]
+    k = np.array([-20, -3, 0, 5], np.int64)
+    rows = rs.choice(grid, size=(4, 256)) * rs.choice([-1.0, 1.0], size=(4, 256))
+    rows[:, 7] = 448.0
+    rows = (rows * np.exp2(k)[:, None]).astype(np.float32)
+    codes, s = oracle.quant_rows_e4m3(rows)
+    assert np.array_equal(s, np.exp2(k).astype(np.float32))
+    assert np.array_equal(oracle.e4m3_to_f64(codes) * s[:, None], rows.astype(np.float64))
+    codes, s = oracle.quant_rows_e4m3(np.zeros((2, 64), np.float32))
+    assert (s == 1.0).all() and (codes == 0).all()
+    v = (rs.standard_normal((64, 1000)) * np.exp(rs.uniform(-30, 30, (64, 1)))).astype(np.float32)
+    codes, s = oracle.quant_rows_e4m3(v)
+    am = np.abs(v).argmax(axis=1)
+    assert (np.abs(oracle.e4m3_to_f64(codes[np.arange(64), am])) == 448.0).all()
+    ncodes, ns = oracle.quant_rows_e4m3(-v)
+    assert np.array_equal(ns, s) and np.array_equal(ncodes, codes ^ 0x80)
+    deq = oracle.act_e4m3(v)
+    sd = s.astype(np.float64)[:, None]
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, sd * 2.0 ** -10) * (1 + 1e-6)
+    assert (np.abs(deq - v) <= bound).all()
+
+
+def test_expert_ffn_act_quant_is_the_quantised_operands():
+    """With act_quant the expert sees E4M3 rows of x and of its BF16-stored SwiGLU
+    output: an x already on the E4M3 grid with amax 448 (scale 1) goes through unchanged,
+    so the first product equals the unquantised one; the output then moves by no more
+    than the E4M3 step of a (2^-4 relative per entry) allows."""
+    rs = np.random.default_rng(8)
+    H, I = 64, 32
+    grid = oracle.E4M3_TABLE[:0x7F] / 448.0
+    x = rs.choice(grid, size=(5, H)) * rs.choice([-1.0, 1.0], size=(5, H))
+    x[:, 0] = 1.0
+    x = (x * 448.0).astype(np.float32)                       # amax 448: scale 1
+    assert np.array_equal(oracle.act_e4m3(x), x.astype(np.float64))
+    w13 = rs.standard_normal((2 * I, H)) / 8 / np.sqrt(H) / 448
+    w2 = rs.standard_normal((H, I)) / np.sqrt(I)
+    y = oracle.expert_ffn(x.astype(np.float64), w13, w2)
+    yq = oracle.expert_ffn(x.astype(np.float64), w13, w2, act_quant=True)
+    g = x.astype(np.float64) @ w13[:I].T
+    a = oracle.silu(g) * (x.astype(np.float64) @ w13[I:].T)
+    bound = (np.abs(a) * (2.0 ** -4 + 2.0 ** -8) + np.abs(a).max(1, keepdims=True) * 2.0 ** -18) @ np.abs(w2.T)
+    assert (np.abs(yq - y) <= bound).all()
+    assert not np.array_equal(yq, y)
+
+
 def test_bf16_widening_matches_torch():
     import torch
     bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
