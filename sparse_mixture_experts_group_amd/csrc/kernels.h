@@ -35,8 +35,8 @@ constexpr int kDenseStreamMaxT = 16;   // the dense MLP (all rows on one weight 
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
 // chunk sums) below 4096 tokens, where it fills the chip and the tiled kernel cannot,
-// and the register-tiled kernel from there on; the tiled kernel stages whole multiples
-// of 16 hidden entries of one chunk (H / 64 % 16 == 0).
+// and the matrix-core kernel from there on; that kernel stages whole multiples of 16
+// hidden entries of one chunk (H / 64 % 16 == 0) and whole 128-expert blocks.
 inline bool router_uses_partials(int64_t T, int H, int E) {
     return !(E % 128 == 0 && T >= 4096 && (H / 64) % 16 == 0);
 }

@@ -294,6 +294,32 @@ def test_select_bias_beam_routing(T):
             assert np.array_equal(np.sort(rid, axis=1), np.tile(np.sort(forced), (T, 1)))
 
 
+@pytest.mark.parametrize("act,T", [("f32", 4096), ("f32", 16384), ("f32", 16385), ("bf16", 16400), ("bf16", 8191)])
+def test_matrix_core_router_logits_bit_exact(act, T):
+    """The matrix-core logits kernel in both of its shapes (32-expert wave tiles below
+    16384 tokens, 64-expert ones from there) with FP32 and BF16 tokens, ragged token
+    counts included: logits bit for bit, then ids and weights, Beam-sized router with
+    logit offsets."""
+    from dataclasses import replace
+    from beam_inputs import token_inputs, to_bf16_bits
+    w0, full, dev, _, bias = gpu_inputs("beam_prefill_t4096")
+    # FP32 tokens need an FP32 layer config (routing reads no expert weights)
+    w = replace(w0, T=T, x_recipe="normal", **(dict(act_dtype=DT_F32, weight_dtype=DT_F32) if act == "f32" else {}))
+    xt = token_inputs(w)
+    x = xt.astype(np.float32) if act == "f32" else to_bf16_bits(xt)
+    print(f"[case] matrix-core router {act} T={T}", flush=True)
+    cfg = cfg_of(w)
+    ws = bm.alloc_workspace(cfg, T)
+    ids, wts = bm.beam_moe_route(cfg, to_dev_x(w, x), dev["w_router"], logit_bias=dev_bias(bias), ws=ws)
+    torch.cuda.synchronize()
+    z_ref = oracle.router_logits(x_f32(w, x), full.w_router, bias)
+    z = ws_region(ws, bm.beam_moe_workspace_map(cfg, T)["logits"], T * w.E, np.float32).reshape(T, w.E)
+    bad = int((z.view(np.uint32) != z_ref.view(np.uint32)).sum())
+    assert bad == 0, f"{bad} logits differ"
+    rid, rw = oracle.route(z_ref, w.G, w.Kg, w.K, w.alpha)
+    check_routing(w, ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+
+
 def test_router_all_ties_and_duplicated_columns():
     """W_r = 0: every score ties (ids 0..K-1, weights alpha/K).  Duplicated W_r columns
     across groups: exact equal scores across groups resolved toward lower indices."""
