@@ -17,6 +17,8 @@
 #include "common.cuh"
 #include "kernels.h"
 
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
 namespace beam {
 
 // ---------------------------------------------------------------------------
@@ -437,20 +439,29 @@ done:
 // ---------------------------------------------------------------------------
 // permutation: per-expert counts, offsets, tile list, active-expert list
 // ---------------------------------------------------------------------------
+// Exclusive prefix sum over the 256 threads of a block (4 waves) in thread order, and the
+// total: a shuffle scan inside each wave, the 4 wave totals through LDS (sh[0..3]), two
+// barriers (the second so the next call may reuse sh).  Integer sums: exact in any order.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int add = tid >= o ? sh[tid - o] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
     }
-    const int incl = sh[tid];
-    total = sh[255];
+    if (lane == 63) sh[wave] = x;
     __syncthreads();
-    return incl - v;
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int t = sh[w];
+        before += w < wave ? t : 0;
+        tot += t;
+    }
+    total = tot;
+    __syncthreads();
+    return before + x - v;
 }
 
 // Column scan: block e turns the selection blocks' counts of expert e into exclusive
@@ -477,22 +488,22 @@ __global__ __launch_bounds__(256) void route_col_scan(int nblk, int E, const int
 // with the same count sit together, so when no expert has more than two tiles (a few
 // hundred rows per expert) every two-tile expert starts at an even index: its two tiles
 // fall in one group of row tiles that an XCD runs side by side (the GEMMs' block order),
-// and the second reads each weight panel from that XCD's L2.  s_nt: the tile counts of
-// all kMaxExperts slots in LDS, zero past E (written and synchronised by the caller).
-// Every thread reads all of them, four per LDS read with the reads unrolled, so they are
-// in flight together (a loop of dependent single reads took ~20 us at E = 256).
+// and the second reads each weight panel from that XCD's L2.  s_key: for every one of the
+// kMaxExperts slots i, its tile count n_i times 256 plus 255 - i (0 tiles past E), so one
+// comparison of keys gives the order; the base is the sum of n_i over the larger keys.
+// Every thread reads all keys, four per LDS read, several reads in flight.
 static_assert(kMaxExperts == 256, "the scan kernels run one thread per expert slot (256 threads)");
-__device__ __forceinline__ int tile_list_base(int e, int nt, const int* s_nt) {
-    const int4* v = reinterpret_cast<const int4*>(s_nt);
+__device__ __forceinline__ int tile_key(int e, int nt) { return nt * 256 + (255 - e); }
+__device__ __forceinline__ int tile_list_base(int key, const int* s_key) {
+    const int4* v = reinterpret_cast<const int4*>(s_key);
     int base = 0;
-#pragma unroll 16
+#pragma unroll 8
     for (int q = 0; q < kMaxExperts / 4; ++q) {
         const int4 c = v[q];
-        const int i = 4 * q;
-        base += (c.x > nt || (c.x == nt && i < e)) ? c.x : 0;
-        base += (c.y > nt || (c.y == nt && i + 1 < e)) ? c.y : 0;
-        base += (c.z > nt || (c.z == nt && i + 2 < e)) ? c.z : 0;
-        base += (c.w > nt || (c.w == nt && i + 3 < e)) ? c.w : 0;
+        base += c.x > key ? c.x >> 8 : 0;
+        base += c.y > key ? c.y >> 8 : 0;
+        base += c.z > key ? c.z >> 8 : 0;
+        base += c.w > key ? c.w >> 8 : 0;
     }
     return base;
 }
@@ -510,11 +521,11 @@ __global__ __launch_bounds__(256) void route_scan(int E, int BM, const int32_t* 
     if (e < E) exp_off[e] = base;
     if (e == 0) exp_off[E] = total_rows;
     const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
-    __shared__ __attribute__((aligned(16))) int s_nt[kMaxExperts];
-    s_nt[e] = nt;                                     // 256 threads: every slot, 0 past E
+    __shared__ __attribute__((aligned(16))) int s_key[kMaxExperts];
+    s_key[e] = tile_key(e, nt);                       // 256 threads: every slot, 0 tiles past E
     int total_tiles;
-    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_nt)
-    const int tbase = tile_list_base(e, nt, s_nt);
+    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_key)
+    const int tbase = tile_list_base(tile_key(e, nt), s_key);
     for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
@@ -555,11 +566,11 @@ __global__ __launch_bounds__(256) void route_finish_small(int T, int K, int E, i
     if (e < E) { exp_off[e] = base; s_off[e] = base; }
     if (e == 0) exp_off[E] = total_rows;
     const int nt = (e < E) ? expert_tile_count(tot, BM) : 0;
-    __shared__ __attribute__((aligned(16))) int s_nt[kMaxExperts];
-    s_nt[e] = nt;                                     // 256 threads: every slot, 0 past E
+    __shared__ __attribute__((aligned(16))) int s_key[kMaxExperts];
+    s_key[e] = tile_key(e, nt);                       // 256 threads: every slot, 0 tiles past E
     int total_tiles;
-    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_nt)
-    const int tbase = tile_list_base(e, nt, s_nt);
+    block_exclusive_scan(nt, sh, total_tiles);       // (its barriers also publish s_key)
+    const int tbase = tile_list_base(tile_key(e, nt), s_key);
     for (int j = 0; j < nt; ++j) tiles[tbase + j] = make_int2(e, j);
     int n_active;
     const int abase = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sh, n_active);
