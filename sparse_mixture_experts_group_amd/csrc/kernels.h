@@ -34,11 +34,14 @@ constexpr int kFp8GateUpStreamMaxT = 16, kFp8DownStreamMaxT = 103;
 constexpr int kDenseStreamMaxT = 16;   // the dense MLP (all rows on one weight set), both GEMMs
 
 // The router logits use the chunk-parallel kernel (with a [64, T, E] FP32 scratch of
-// chunk sums) below 4096 tokens, where it fills the chip and the tiled kernel cannot,
-// and the matrix-core kernel from there on; that kernel stages whole multiples of 16
-// hidden entries of one chunk (H / 64 % 16 == 0) and whole 128-expert blocks.
+// chunk sums) below 1536 tokens and the matrix-core kernel from there on; the latter
+// stages whole multiples of 16 hidden entries of one chunk (H / 64 % 16 == 0) and whole
+// 128-expert blocks.  Measured crossover on the Beam router (one MI355X): 1024 tokens
+// 0.11 against 0.13-0.14 ms, 1536 tokens 0.16 against 0.13-0.14, 4095 tokens 0.48
+// against 0.23-0.26 (the matrix-core kernel's time is nearly flat below 2048 tokens,
+// where it holds fewer waves than SIMDs).
 inline bool router_uses_partials(int64_t T, int H, int E) {
-    return !(E % 128 == 0 && T >= 4096 && (H / 64) % 16 == 0);
+    return !(E % 128 == 0 && T >= 1536 && (H / 64) % 16 == 0);
 }
 
 inline int scores_per_lane(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }

@@ -294,12 +294,13 @@ def test_select_bias_beam_routing(T):
             assert np.array_equal(np.sort(rid, axis=1), np.tile(np.sort(forced), (T, 1)))
 
 
-@pytest.mark.parametrize("act,T", [("f32", 4096), ("f32", 16384), ("f32", 16385), ("bf16", 16400), ("bf16", 8191)])
+@pytest.mark.parametrize("act,T", [("bf16", 1535), ("bf16", 1536), ("f32", 1537), ("f32", 4096), ("f32", 16384),
+                                   ("f32", 16385), ("bf16", 16400), ("bf16", 8191)])
 def test_matrix_core_router_logits_bit_exact(act, T):
-    """The matrix-core logits kernel in both of its shapes (32-expert wave tiles below
-    16384 tokens, 64-expert ones from there) with FP32 and BF16 tokens, ragged token
-    counts included: logits bit for bit, then ids and weights, Beam-sized router with
-    logit offsets."""
+    """The matrix-core logits kernel in both of its shapes (32-expert wave tiles from
+    1536 tokens, 64-expert ones from 16384) with FP32 and BF16 tokens, ragged token
+    counts included, and the chunk-parallel kernel just below its crossover: logits bit
+    for bit, then ids and weights, Beam-sized router with logit offsets."""
     from dataclasses import replace
     from beam_inputs import token_inputs, to_bf16_bits
     w0, full, dev, _, bias = gpu_inputs("beam_prefill_t4096")
