@@ -283,13 +283,13 @@ int beam_dense_sublayer_forward(const beam_moe_config* cfg, int64_t T, void* h,
 
 /*
  * Kernel timing hook (instrumentation for benchmarks; not needed for computing).
- * After this call, every launch of the selected kernel by later calls in this process
- * is bracketed by hipEventRecord of the next pair of events on the launch stream:
+ * After this call, every launch of the selected kernel by later calls from the same host
+ * thread is bracketed by hipEventRecord of the next pair of events on the launch stream:
  * launch i records events[2i] before and events[2i+1] after the kernel, for i < n_pairs;
  * later launches are not bracketed.  `events` holds hipEvent_t handles created by the
  * caller (with timing enabled) and must stay valid until the last bracketed launch has
- * been recorded.  kernel: BEAM_KERNEL_NONE disables the hook.  The hook is process-wide
- * state: calls from several threads while it is armed race on the pair index.
+ * been recorded.  kernel: BEAM_KERNEL_NONE disables the hook.  The hook belongs to the
+ * calling host thread: calls from other threads are neither bracketed nor disturbed.
  * Returns BEAM_ERR_INVALID_ARG for an unknown kernel id, n_pairs < 0, or events == NULL
  * with n_pairs > 0.
  */

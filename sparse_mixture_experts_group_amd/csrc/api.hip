@@ -176,14 +176,15 @@ int check_ws(const beam_moe_config* cfg, int64_t T, void* ws, size_t ws_bytes) {
     return BEAM_OK;
 }
 
-// Kernel timing hook state (see beam_moe_time_kernel).
+// Kernel timing hook state (see beam_moe_time_kernel): one per host thread, so threads
+// that drive different devices (or streams) time their own launches without racing.
 struct TimingHook {
     int kernel = BEAM_KERNEL_NONE;
     void* const* events = nullptr;
     int n_pairs = 0;
     int next = 0;
 };
-TimingHook g_hook;
+thread_local TimingHook g_hook;
 
 struct Bracket {
     hipStream_t st;
