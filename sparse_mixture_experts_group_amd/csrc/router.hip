@@ -120,22 +120,30 @@ __global__ __launch_bounds__(256) void router_logits_reduce(int T, int E, const 
     z[idx] = tot;
 }
 
-// Large T on the matrix cores.  v_mfma_f32_32x32x1_2b_f32 adds one product per output
-// to its accumulator and rounds once, as an FMA does (checked bit for bit against an
+// Large T on the matrix cores.  The FP32 MFMAs with one K value per instruction
+// (v_mfma_f32_32x32x1_2b_f32, v_mfma_f32_16x16x1_4b_f32) add one product per output to
+// its accumulator and round once, as an FMA does (checked bit for bit against an exact
 // IEEE fma chain on gfx950, denormals included), so a run of them over k is each chunk's
 // fma chain in the contract's order, at the FP32 matrix rate (twice the vector FMA rate
-// without packed FP32).  The instruction's two 32 x 32 blocks are the two 32-expert
-// halves of a wave's 64 experts: lane l gives token l % 32's x[t, k] as the A value and
-// expert l's w[k, e] as the B value, and accumulator r of lane l holds block b = r / 16,
-// token 8 ((r % 16) / 4) + 4 (l / 32) + r % 4, expert 32 b + l % 32.
-// Wave tile: 32 NS tokens x 64 experts (NS token sets share the B values); block: NW
+// without packed FP32).
+// Shapes (lane l, accumulator r):
+//   32 x 32 (M16 false): the instruction's two 32 x 32 blocks are the two 32-expert
+//     halves of the wave's 64 experts; lane l gives token l % 32's x[t, k] as A and expert
+//     l's w[k, e] as B; r holds block r / 16, token 8 ((r % 16) / 4) + 4 (l / 32) + r % 4,
+//     expert 32 (r / 16) + l % 32.
+//   16 x 16 (M16 true): the four 16 x 16 blocks b are (token half b % 2, expert half
+//     b / 2) of 32 tokens x 32 experts (an expert set; WE / 32 sets per wave); lane l gives
+//     token l % 32 as A and expert 16 (l / 32) + l % 16 of the set as B; r holds block
+//     r / 4, token 4 (l / 16) + r % 4 of its half, expert l % 16 of its half.
+// Wave tile: 32 NS tokens x WE experts (the NS token sets share the B values); block: NW
 // waves side by side along the experts.  Tiles of 16 hidden entries (a divisor of the
 // chunk length H / 64) stream through a ring of S LDS stages filled by direct-to-LDS
-// loads, S - 1 tiles ahead: w as [16][64 NW] FP32 (one float per lane and k), x as its
+// loads, S - 1 tiles ahead: w as [16][WE NW] FP32 (one float per lane and k), x as its
 // rows of 16 entries (BF16 or FP32, converted when read; 16-byte pieces of a row placed
 // in swizzled slots so the fragment reads of 32 rows spread over the banks).  Every wave
-// moves 4 KB of w and BT / NW rows of x per stage, so all waves wait for fixed counts.
-// After each chunk's tiles, each accumulator is added to its running sum and cleared.
+// moves WE / 16 KB of w and 32 NS / NW rows of x per stage, so all waves wait for fixed
+// counts.  After each chunk's tiles, each accumulator is added to its running sum (FP32,
+// chunk order) and cleared.
 template <bool XBF16, int WE, bool M16, int NS, int NW, int S>
 __global__ __launch_bounds__(64 * NW) void router_logits_mfma(int T, int H, int E, const void* x,
                                                               const float* __restrict__ wr,
