@@ -185,7 +185,9 @@ __device__ __forceinline__ void load8(const void* src, int64_t i, float* v) {
     }
 }
 
-template <bool SRC_BF16>
+// MC > 0: rows of at most MC * 512 columns are read once into registers (8 columns per
+// lane and chunk), so the quantising pass does not read them again; MC = 0: two passes.
+template <bool SRC_BF16, int MC>
 __global__ __launch_bounds__(256) void quant_rows_fp8(int64_t rows, int cols, const void* __restrict__ src,
                                                       uint8_t* __restrict__ q, float* __restrict__ scale) {
     const int lane = threadIdx.x & 63;
@@ -193,6 +195,33 @@ __global__ __launch_bounds__(256) void quant_rows_fp8(int64_t rows, int cols, co
     if (r >= rows) return;
     const int64_t base = r * cols;
     float am = 0.0f;
+    if constexpr (MC > 0) {
+        float v[MC][8];
+#pragma unroll
+        for (int k = 0; k < MC; ++k) {
+            const int c = (lane + 64 * k) * 8;
+            if (c < cols) {
+                load8<SRC_BF16>(src, base + c, v[k]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[k][j]));
+            }
+        }
+        am = wave_max(am);
+        const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+        const float inv = 1.0f / sc;
+#pragma unroll
+        for (int k = 0; k < MC; ++k) {
+            const int c = (lane + 64 * k) * 8;
+            if (c < cols) {
+                u32x2 o;
+                o[0] = f32x4_to_e4m3x4(v[k][0] * inv, v[k][1] * inv, v[k][2] * inv, v[k][3] * inv);
+                o[1] = f32x4_to_e4m3x4(v[k][4] * inv, v[k][5] * inv, v[k][6] * inv, v[k][7] * inv);
+                *reinterpret_cast<u32x2*>(q + base + c) = o;
+            }
+        }
+        if (lane == 0) scale[r] = sc;
+        return;
+    }
     for (int c = lane * 8; c < cols; c += 512) {
         float v[8];
         load8<SRC_BF16>(src, base + c, v);
@@ -217,8 +246,14 @@ void launch_quant_rows_fp8(hipStream_t st, int64_t rows, int cols, bool src_bf16
                            const void* src, uint8_t* q, float* scale) {
     if (rows == 0) return;
     const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
-    if (src_bf16) quant_rows_fp8<true><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
-    else quant_rows_fp8<false><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+    // one register pass up to 5120 columns (Beam's hidden size and SwiGLU width)
+    if (cols <= 10 * 512) {
+        if (src_bf16) quant_rows_fp8<true, 10><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+        else quant_rows_fp8<false, 10><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+    } else {
+        if (src_bf16) quant_rows_fp8<true, 0><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+        else quant_rows_fp8<false, 0><<<blocks, 256, 0, st>>>(rows, cols, src, q, scale);
+    }
 }
 
 // ---------------------------------------------------------------------------
