@@ -123,6 +123,11 @@ def rel_inf(got, ref):
     return float(np.abs(got - ref).max() / np.abs(ref).max())
 
 
+def rel_rms(got, ref):
+    """RMS relative error sqrt(mean((got - ref)^2) / mean(ref^2)), reported beside rel_inf."""
+    return float(np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2)))
+
+
 def sample_tokens(T, n=16, seed=1):
     """Tokens 0, T/2 and T-1 plus n distinct random others."""
     rs = np.random.default_rng(seed)
@@ -179,11 +184,12 @@ def check_expert_rows(w, ws, rows, yref_rows, tol):
 
 def layer_errors(w, cfg, ws, y, x32, tok, rid, rw, bank):
     """Layer output of tokens `tok` against the oracle with plain and with E4M3
-    operands, one pass over the experts."""
+    operands, one pass over the experts (RMS relative errors printed beside)."""
     outs, outs_q, _, _ = expert_refs(bank, x32[tok].astype(np.float64), rid[tok])
     got = y.float().cpu().numpy()[tok].astype(np.float64)
-    return (rel_inf(got, oracle.combine_outputs(outs, rw[tok])),
-            rel_inf(got, oracle.combine_outputs(outs_q, rw[tok])))
+    ref, ref_q = oracle.combine_outputs(outs, rw[tok]), oracle.combine_outputs(outs_q, rw[tok])
+    print(f"[case] rel_rms plain {rel_rms(got, ref):.3e}, E4M3 operands {rel_rms(got, ref_q):.3e}", flush=True)
+    return rel_inf(got, ref), rel_inf(got, ref_q)
 
 
 def run_forward(w, dev, x, bias, select_bias=None, declared=None):
@@ -385,8 +391,8 @@ def test_beam_bf16_layer(name, T):
     rop = ws_region(ws, bm.beam_moe_workspace_map(cfg, w.T)["row_of_pair"], w.T * w.K, np.int32)
     prow = rop.reshape(w.T, w.K)[tok].reshape(-1)
     e_rows = check_expert_rows(w, ws, prow, outs.reshape(-1, w.H), TOL[w.weight_dtype])
-    print(f"[case] {name} T={w.T} tokens={len(tok)} rel_inf={err:.3e} expert rows={len(prow)} "
-          f"rel_inf={e_rows:.3e}", flush=True)
+    print(f"[case] {name} T={w.T} tokens={len(tok)} rel_inf={err:.3e} rel_rms={rel_rms(yg, yref):.3e} "
+          f"expert rows={len(prow)} rel_inf={e_rows:.3e}", flush=True)
     assert err <= TOL[w.weight_dtype]
 
 
@@ -468,6 +474,9 @@ def test_fp8_sublayer(name):
         y_ref = oracle.combine_outputs(o, rw[tok])
         res[name] = (rel_inf(y_got, y_ref), rel_inf(h_got, oracle.sublayer_output(h32[tok], y_ref, None, w.step_k,
                                                                                   w.norm_eps)))
+    print(f"[case] sublayer fp8 {w.fp8_scales} rel_rms moe: plain "
+          f"{rel_rms(y_got, oracle.combine_outputs(outs, rw[tok])):.3e}, E4M3 operands "
+          f"{rel_rms(y_got, oracle.combine_outputs(outs_q, rw[tok])):.3e}", flush=True)
     print(f"[case] sublayer fp8 {w.fp8_scales} tokens={len(tok)} gate/up rows rel_inf={e_gu:.3e} "
           f"down rows rel_inf={e_dn:.3e} (plain oracle {e_rows:.3e}); moe, h rel_inf: plain "
           f"{res['plain'][0]:.3e}, {res['plain'][1]:.3e}; E4M3 operands {res['E4M3 operands'][0]:.3e}, "
