@@ -23,6 +23,12 @@ constant scale"):
 The router and the pre-norm are FP32 because the pages fix those sites to FP32
 and their result decides integers (expert ids); every other step is float64, a
 tighter reference than the FP32 floor the pages set.
+
+Optional operand model for 8-bit expert weights (`ExpertBank(act_quant=True)`): the
+GEMMs' activation operands as E4M3 rows with an FP32 amax/448 scale, x as given and the
+SwiGLU output after FP32 and BF16 rounding (`quant_rows_e4m3`, `bf16_round`); products
+and sums stay float64.  The pages name FP8 checkpoints but not the activation format,
+so this is a reading; tests compare the GPU against the oracle with and without it.
 """
 from __future__ import annotations
 
